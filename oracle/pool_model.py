@@ -1,0 +1,166 @@
+"""Pure-Python model of the paged KV block pool (test infrastructure only).
+
+What the pages fix:
+  * KV blocks of a fixed number of tokens; a sequence's logical blocks map to
+    physical blocks anywhere in the pool through a per-request block table that
+    also records how many positions are filled (vLLM encyclopedia entry,
+    tonho.wtf, section "como funciona"; "KV Cache Administration", section
+    "How PagedAttention Works", steps 1 and 2).
+  * A new physical block is taken only when the previous one is full, so a
+    request wastes at most one block (same section; the briefia.fr explainer,
+    section "PagedAttention traite la mémoire").
+  * Parallel samples map the prompt blocks with a reference count equal to the
+    number of holders; a write into the shared last block copies that block and
+    only that block (tonho.wtf, "como funciona"; copy-on-write in all three
+    explainers).  Everything is expressed with fork, append and free.
+
+What the pages leave open, fixed here so that tables are reproducible bit for
+bit (the C++ pool implements the same policy):
+  * free list: FIFO; initial order given by the caller; a block whose refcount
+    drops to zero goes to the back;
+  * free(seq) releases its blocks in logical order;
+  * append(seq, k): a copy happens only on the first token of a call, when the
+    sequence's fill is not a multiple of block_size and its last block is held
+    by another sequence; the appending sequence copies, the last holder writes
+    in place;
+  * append is all-or-nothing: if the free list cannot cover the call, nothing
+    changes and NO_BLOCKS is returned; a batch append is all-or-nothing over the
+    whole batch, processed in the order given.
+"""
+from __future__ import annotations
+
+from collections import deque
+
+OK, INVALID, UNSUPPORTED, NO_BLOCKS, UNKNOWN_SEQ = 0, 1, 2, 3, 4
+
+
+class PoolModel:
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("bad pool size")
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise ValueError("free_order must be a permutation")
+        self.num_blocks = num_blocks
+        self.bs = block_size
+        self.free = deque(order)
+        self.ref = [0] * num_blocks
+        self.tables: dict[int, list[int]] = {}
+        self.fill: dict[int, int] = {}
+        self.copies = 0
+
+    # -- block primitives ----------------------------------------------------
+    def _alloc(self) -> int:
+        b = self.free.popleft()
+        self.ref[b] = 1
+        return b
+
+    def _release(self, b: int):
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self.free.append(b)
+
+    # -- sequence operations -------------------------------------------------
+    def create(self, sid: int) -> int:
+        if sid in self.tables:
+            return INVALID
+        self.tables[sid] = []
+        self.fill[sid] = 0
+        return OK
+
+    def fork(self, parent: int, child: int) -> int:
+        if parent not in self.tables:
+            return UNKNOWN_SEQ
+        if child in self.tables:
+            return INVALID
+        self.tables[child] = list(self.tables[parent])
+        self.fill[child] = self.fill[parent]
+        for b in self.tables[child]:
+            self.ref[b] += 1
+        return OK
+
+    def free_seq(self, sid: int) -> int:
+        if sid not in self.tables:
+            return UNKNOWN_SEQ
+        for b in self.tables.pop(sid):
+            self._release(b)
+        del self.fill[sid]
+        return OK
+
+    def _needed(self, sid: int, k: int, ref) -> int:
+        """Blocks that append(sid, k) takes, given refcounts `ref`."""
+        n = self.fill[sid]
+        if k == 0:
+            return 0
+        need = sum(1 for pos in range(n, n + k) if pos % self.bs == 0)
+        if n % self.bs != 0 and ref[self.tables[sid][-1]] > 1:
+            need += 1
+        return need
+
+    def _append_one_call(self, sid: int, k: int, slots: list, pairs: list):
+        table = self.tables[sid]
+        for j in range(k):
+            n = self.fill[sid]
+            if n % self.bs == 0:
+                table.append(self._alloc())
+            elif j == 0 and self.ref[table[-1]] > 1:
+                old = table[-1]
+                new = self._alloc()
+                pairs.append((old, new))
+                self.copies += 1
+                self._release(old)
+                table[-1] = new
+            slots.append(table[-1] * self.bs + n % self.bs)
+            self.fill[sid] = n + 1
+
+    def append(self, sid: int, k: int):
+        """Returns (status, slots, pairs)."""
+        return self.append_batch([sid], k)
+
+    def append_batch(self, sids, k: int):
+        """Append k tokens to each sequence of `sids`, in order.  Returns
+        (status, slots [len(sids)*k], pairs [(src, dst), ...])."""
+        if k < 0:
+            return INVALID, [], []
+        if len(set(sids)) != len(sids):
+            return INVALID, [], []
+        for s in sids:
+            if s not in self.tables:
+                return UNKNOWN_SEQ, [], []
+        # dry run of the refcount changes to count the blocks the batch takes
+        ref = {}
+        need = 0
+        for s in sids:
+            view = _RefView(self.ref, ref)
+            c = self._needed(s, k, view)
+            need += c
+            n = self.fill[s]
+            if k and n % self.bs != 0 and view[self.tables[s][-1]] > 1:
+                ref[self.tables[s][-1]] = view[self.tables[s][-1]] - 1
+        if need > len(self.free):
+            return NO_BLOCKS, [], []
+        slots, pairs = [], []
+        for s in sids:
+            self._append_one_call(s, k, slots, pairs)
+        return OK, slots, pairs
+
+    # -- queries -------------------------------------------------------------
+    def block_table(self, sid: int):
+        return list(self.tables[sid]), self.fill[sid]
+
+    def stats(self):
+        used = sum(1 for r in self.ref if r > 0)
+        shared = sum(1 for r in self.ref if r > 1)
+        tokens = sum(self.fill.values())
+        return {"free": len(self.free), "used": used, "shared": shared,
+                "tokens": tokens, "copies": self.copies}
+
+
+class _RefView:
+    """Refcounts with a sparse overlay of pending changes (dry runs)."""
+
+    def __init__(self, base, overlay):
+        self.base, self.overlay = base, overlay
+
+    def __getitem__(self, b):
+        return self.overlay.get(b, self.base[b])
