@@ -1,0 +1,267 @@
+"""PagedAttention decode benchmark on one MI355X.
+
+One step = the whole decode hot path for one batch: the host pool appends one
+token per sequence (slot mapping and copy-on-write decisions, C++), block
+tables / lengths / slots go to the device through pinned double buffers,
+pa_copy_blocks runs for any copy-on-write pair, pa_write_kv stores the new
+K/V, and pa_decode (partition kernel + log-sum-exp reduce) computes the
+attention output.  Inputs are resident in HBM before the timed region starts.
+
+Prints one JSON line.  `value` is the effective KV bandwidth of the whole step
+(algorithmic KV bytes read by the step's decode / step time);
+`roofline` covers pa_decode alone, timed with HIP events on its stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "llama3_8b_gqa_bf16"
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_12_amd", "csrc", "pa_decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+
+
+def fill_cache(sc, cache, dev):
+    """Run the workload's op script through the product path (C++ pool +
+    pa_copy_blocks + pa_write_kv)."""
+    import torch
+    from paged_kv_cache_12_amd.manager import storage_to_torch
+    dt = sc.wl.dtype
+
+    def put(a):
+        return storage_to_torch(a, dt).to(dev)
+
+    for op in sc.ops:
+        kind = op[0]
+        if kind == "create":
+            cache.create(op[1])
+        elif kind == "fork":
+            cache.fork(op[1], op[2])
+        elif kind == "free":
+            torch.cuda.synchronize()
+            cache.free(op[1])
+        elif kind == "append":
+            run = op[1]
+            if run.ntok:
+                kv, vv = sc.values(run)
+                cache.append([run.seq], run.ntok, put(kv), put(vv))
+        elif kind == "append_rr":
+            runs = [r for r in op[1] if r.ntok > 0]
+            vals = {r.seq: sc.values(r) for r in runs}
+            for rr in range(max((r.ntok for r in runs), default=0)):
+                live = [r.seq for r in runs if r.ntok > rr]
+                kv = np.stack([vals[s][0][rr] for s in live])
+                vv = np.stack([vals[s][1][rr] for s in live])
+                cache.append(live, 1, put(kv), put(vv))
+    torch.cuda.synchronize()
+
+
+def cpu_baseline(sc, budget_s: float):
+    """Time the oracle (as it stands) on a bounded sample of the same workload:
+    its pool model and cache writes set up the sample, then paged_decode over
+    the sample's sequences is repeated until `budget_s` seconds have passed."""
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as A
+    from oracle.pool_model import PoolModel
+    wl = sc.wl
+    B = len(sc.decode_seqs)
+    nsamp = min(B, 8)
+    samp = sc.decode_seqs[:nsamp]
+    model = PoolModel(sc.num_blocks, wl.block_size, sc.free_order)
+    st = synth.STORAGE[wl.dtype]
+    kc = np.zeros(A.k_cache_shape(sc.num_blocks, wl.h_kv, wl.block_size, wl.head_dim, wl.dtype), st)
+    vc = np.zeros(A.v_cache_shape(sc.num_blocks, wl.h_kv, wl.block_size, wl.head_dim, wl.dtype), st)
+    for op in sc.ops:
+        if op[0] == "create" and op[1] in samp:
+            model.create(op[1])
+        elif op[0] == "append" and op[1].seq in samp:
+            kv, vv = sc.values(op[1])
+            _, slots, _ = model.append(op[1].seq, op[1].ntok)
+            A.write_kv(kc, vc, kv, vv, slots)
+    tabs = [model.block_table(s) for s in samp]
+    maxb = max(len(t) for t, _ in tabs)
+    tab = np.full((nsamp, maxb), -1, np.int32)
+    lens = np.array([n for _, n in tabs], np.int32)
+    for i, (t, _) in enumerate(tabs):
+        tab[i, :len(t)] = t
+    q = sc.q[:nsamp]
+    kv_bytes = float(lens.sum()) * 2 * wl.h_kv * wl.head_dim * synth.ELEM_BYTES[wl.dtype]
+    reps = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            A.paged_decode(q, kc, vc, tab, lens, wl.scale, wl.dtype)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    per_step = el / reps
+    return {"value": kv_bytes / per_step / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seq_steps_per_s": nsamp / per_step,
+            "sample": f"{nsamp} of {B} sequences of {wl.name} (ctx {int(lens.min())}-"
+                      f"{int(lens.max())}), fp64 NumPy paged_decode repeated {reps}x over "
+                      f"{el:.1f} s, BLAS limited to 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU "
+              "sharding of this path is design-only.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_12_amd as pa
+    from paged_kv_cache_12_amd.manager import PagedKVCache, storage_to_torch
+    pa.lib()
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    part = wl.partition if args.partition is None else args.partition
+    sc = synth.build_scenario(wl)
+    cache = PagedKVCache(sc.num_blocks, wl.block_size, wl.h_kv, wl.head_dim, wl.dtype,
+                         device=dev, free_order=sc.free_order)
+    fill_cache(sc, cache, dev)
+    seqs = np.asarray(sc.decode_seqs, dtype=np.int64)
+    B = seqs.size
+    e = synth.ELEM_BYTES[wl.dtype]
+    total_steps = args.warmup + args.steps
+    appends = wl.step_append
+
+    # capacity for the run
+    _, lens0 = cache.tables(seqs)
+    max_ctx_end = int(lens0.max()) + (total_steps if appends else 0)
+    maxb = -(-max_ctx_end // wl.block_size)
+    q = storage_to_torch(sc.q, wl.dtype).to(dev)
+    out = torch.empty_like(q)
+    ws_bytes = pa.pa_decode_workspace_size(B, wl.h_q, wl.head_dim, max_ctx_end, part)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    if appends:
+        step_k = storage_to_torch(sc.step_k, wl.dtype).to(dev)
+        step_v = storage_to_torch(sc.step_v, wl.dtype).to(dev)
+
+    # pinned host staging, double buffered
+    nbuf = 2
+    h_tab = [torch.empty((B, maxb), dtype=torch.int32, pin_memory=True) for _ in range(nbuf)]
+    h_len = [torch.empty(B, dtype=torch.int32, pin_memory=True) for _ in range(nbuf)]
+    h_slot = [torch.empty(B, dtype=torch.int64, pin_memory=True) for _ in range(nbuf)]
+    d_tab = [torch.empty((B, maxb), dtype=torch.int32, device=dev) for _ in range(nbuf)]
+    d_len = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(nbuf)]
+    d_slot = [torch.empty(B, dtype=torch.int64, device=dev) for _ in range(nbuf)]
+    copied = [None] * nbuf
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(total_steps)]
+    ctx_bytes = []
+
+    def step(i):
+        j = i % nbuf
+        if copied[j] is not None:
+            copied[j].synchronize()        # host buffer j is free again
+        if appends:
+            st, slots, pairs = cache.pool.append_batch(seqs, 1, slots_out=h_slot[j].numpy())
+            if st != pa.PA_OK:
+                raise pa.PAError(st, "append_batch")
+        else:
+            pairs = ()
+        cache.pool.block_tables(seqs, maxb, out=h_tab[j].numpy(), lens_out=h_len[j].numpy())
+        ctx_bytes.append(float(h_len[j].numpy().sum()) * 2 * wl.h_kv * wl.head_dim * e)
+        max_ctx = int(h_len[j].numpy().max())
+        d_tab[j].copy_(h_tab[j], non_blocking=True)
+        d_len[j].copy_(h_len[j], non_blocking=True)
+        if appends:
+            d_slot[j].copy_(h_slot[j], non_blocking=True)
+        ce = torch.cuda.Event()
+        ce.record(stream)
+        copied[j] = ce
+        if len(pairs):
+            dp = torch.from_numpy(np.ascontiguousarray(pairs)).to(dev, non_blocking=False)
+            pa.pa_copy_blocks(cache.k_cache, cache.v_cache, dp)
+        if appends:
+            pa.pa_write_kv(step_k, step_v, cache.k_cache, cache.v_cache, d_slot[j])
+        ev[i][0].record(stream)
+        pa.pa_decode(out, q, cache.k_cache, cache.v_cache, d_tab[j], d_len[j], max_ctx, wl.scale,
+                     part, workspace=ws)
+        ev[i][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total_steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, total_steps)]
+    dec_ms_mean = float(np.mean(dec_ms))
+    kv_step = float(np.mean(ctx_bytes[args.warmup:]))
+    value = kv_step / (ms_step * 1e-3) / 1e9
+    achieved = kv_step / (dec_ms_mean * 1e-3) / 1e9
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    if os.path.exists(tfile):
+        t = json.load(open(tfile))
+        if t.get("decode_source_sha256_16") == source_hash() and t.get("partition") == part:
+            traffic = t.get("bytes_per_launch")
+
+    res = {
+        "metric": "paged-attn decode: effective KV HBM GB/s (% of peak) + seq-steps/sec",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) K/V/q, no weights)",
+        "config": {"workload": wl.name, "batch": B, "q_heads": wl.h_q, "kv_heads": wl.h_kv,
+                   "head_dim": wl.head_dim, "block_size": wl.block_size, "partition": part,
+                   "mean_context": round(kv_step / (2 * wl.h_kv * wl.head_dim * e) / B, 1),
+                   "step": ("append 1 token/seq + " if appends else "") + "decode",
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seq_steps_per_s": round(B / (ms_step * 1e-3), 1),
+        "decode_ms_mean": round(dec_ms_mean, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "pa_decode (partition + reduce)",
+                     "bytes_per_launch": round(kv_step)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(sc, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

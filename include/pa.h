@@ -1,0 +1,231 @@
+/*
+ * pa.h — PagedAttention decode for AMD MI355X (gfx950): the C ABI of libpa.so.
+ *
+ * The operations follow the vLLM encyclopedia entry (tonho.wtf): section
+ * "como funciona" (KV blocks of a fixed number of tokens, 16 by default; a
+ * per-request block table mapping logical to physical blocks with a fill
+ * count; a new block only when the previous one is full; reference counts and
+ * copy-on-write for parallel samples; everything expressed as fork, append and
+ * free; decode attention computed block by block) and section "o que isso
+ * custou" (three custom kernels: block write, block read fused with attention,
+ * batched block copy).  "KV Cache Administration: PagedAttention &
+ * RadixAttention" (techtrendfeed), section "How PagedAttention Works", steps
+ * 1-4, and the two other explainers (aitalk.it, briefia.fr) describe the same
+ * mechanism with blocks of 16 or 32 tokens.
+ *
+ * Conventions
+ *  - Every entry point returns a pa_status; no exception crosses the ABI.
+ *  - Scalar and shape arguments are checked before anything is launched:
+ *    PA_ERR_INVALID for null pointers, negative counts, H_q % H_kv != 0, a
+ *    partition size that is not a multiple of 32 tokens, too small a workspace;
+ *    PA_ERR_UNSUPPORTED for head_dim not in {64, 128}, block_size not in
+ *    {16, 32}, or a dtype outside pa_dtype.
+ *  - Device entry points take caller-owned device pointers, never allocate or
+ *    free device memory, and are asynchronous on `stream` (a hipStream_t passed
+ *    as void*; NULL is the default stream).  A launch failure returns
+ *    PA_ERR_HIP.  The caller synchronises.
+ *  - Element contents (slot values, block-table entries) are the caller's
+ *    contract.  Kernels never access memory outside the arrays described by the
+ *    size arguments: out-of-range slots and copy pairs are skipped, and
+ *    out-of-range block-table entries are read as block 0 (wrong output, no
+ *    fault).
+ *  - The host pool is single-owner and not thread-safe (one central block
+ *    manager, as in the encyclopedia entry's section "como funciona").
+ *
+ * Cache layout (the pages fix none; this is the library's).  With
+ * x = 16 / element_bytes (8 for fp16 and bf16, 4 for fp32), one (block, head)
+ * tile is block_size * head_dim contiguous elements, and
+ *   K cache [num_blocks][H_kv][head_dim/x][block_size][x]
+ *       K(block b, head h, token t, dim i) at [b][h][i/x][t][i%x]
+ *   V cache [num_blocks][H_kv][block_size/x][head_dim][x]
+ *       V(block b, head h, token t, dim i) at [b][h][t/x][i][t%x]
+ * Both are built from 16-byte vectors: a K vector holds x consecutive dims of
+ * one token, a V vector holds x consecutive tokens of one dim, which are the
+ * operand shapes of the decode kernel's QK and PV matrix products.
+ *
+ * Slot: slot = physical_block * block_size + offset_in_block.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = 1,
+  PA_ERR_UNSUPPORTED = 2,
+  PA_ERR_NO_BLOCKS = 3,
+  PA_ERR_UNKNOWN_SEQ = 4,
+  PA_ERR_HIP = 5
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Static text for a status code; "unknown status" for other values. */
+const char* pa_status_str(int status);
+
+/* ABI version of this header (incremented on incompatible change). */
+int pa_abi_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Device operations                                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * pa_write_kv — block write: store the K and V of new tokens into the paged
+ * cache (encyclopedia entry, "o que isso custou": the block-write kernel;
+ * "como funciona": blocks are filled left to right through the block table).
+ *
+ *   k_new, v_new  device, [num_tokens][num_kv_heads][head_dim], dtype
+ *   k_cache, v_cache  device, layout above, num_blocks blocks
+ *   slot_mapping  device, int64 [num_tokens]; token j goes to slot_mapping[j].
+ *                 Negative slots and slots >= num_blocks * block_size are
+ *                 skipped.  Slots must be distinct (else the winner is
+ *                 unspecified).
+ * num_tokens == 0 is a no-op.  Bit-exact copy of the element bits.
+ */
+pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      const int64_t* slot_mapping, int num_tokens, int num_blocks,
+                      int num_kv_heads, int head_dim, int block_size, int dtype,
+                      void* stream);
+
+/*
+ * pa_copy_blocks — batched block copy for copy-on-write (encyclopedia entry,
+ * "como funciona": a write into a shared last block copies that block and
+ * only it; "o que isso custou": the batched block-copy kernel).
+ *
+ *   pairs  device, int32 [num_pairs][2] = {src, dst} physical block ids.
+ *          For each pair the whole block (all heads, all positions, K and V)
+ *          of src is copied to dst.  No dst may equal any src or another dst
+ *          of the same call (copies run concurrently).  Pairs with an id
+ *          outside [0, num_blocks) are skipped.
+ * num_pairs == 0 is a no-op.  Bit-exact.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
+                         int num_blocks, int num_kv_heads, int head_dim, int block_size,
+                         int dtype, void* stream);
+
+/*
+ * Bytes of workspace pa_decode needs for these sizes; 0 when no sequence can
+ * span more than one partition (partition_size == 0 or
+ * max_context_len <= partition_size).
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
+                                int max_context_len, int partition_size);
+
+/*
+ * pa_decode — single-query decode attention over block tables (encyclopedia
+ * entry, "como funciona": the current token's query times one block's keys
+ * gives that slice of the scores, and the output is accumulated against the
+ * same block's values; blocks need not be adjacent; "onde isso aparece hoje":
+ * K/V shared between query heads as in GQA).
+ *
+ *   out  device [num_seqs][num_q_heads][head_dim], dtype (written)
+ *   q    device [num_seqs][num_q_heads][head_dim], dtype
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries at
+ *        index >= ceil(context_lens[s] / block_size) are never read
+ *   context_lens  device int32 [num_seqs]; must be <= max_context_len
+ *        (larger values are clamped to it) and <= max_blocks_per_seq*block_size
+ *   scale  softmax scale (1/sqrt(head_dim) for standard attention)
+ *   partition_size  0: one work unit per (sequence, KV head); otherwise the
+ *        context is split into partitions of this many tokens (a multiple of
+ *        32) whose partial results (running max, sum, unnormalised output)
+ *        are merged by a log-sum-exp reduce in ascending partition order
+ *   workspace  device, >= pa_decode_workspace_size(...) bytes (may be NULL
+ *        when that is 0); contents on entry are ignored
+ *
+ * out[s][h] = softmax(scale * q[s][h] . K_s[:, h/G]) V_s[:, h/G], G = H_q/H_kv,
+ * where K_s, V_s are the sequence's tokens in logical order.  A sequence with
+ * context length 0 gets a zero row.  fp32 accumulation; the PV product of the
+ * fp16/bf16 path rounds the softmax weights to the input dtype.  The result is
+ * deterministic (no atomics; fixed reduction order).
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens, int num_seqs, int max_context_len,
+                    int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                    int num_blocks, float scale, int partition_size, void* workspace,
+                    size_t workspace_bytes, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block pool (host memory only; no HIP calls)                          */
+/* ------------------------------------------------------------------------ */
+/*
+ * Policy (the pages give the operations, not an order; this one is fixed so
+ * that tables are reproducible): the free list is FIFO, initialised to
+ * free_order (or 0..num_blocks-1 when NULL); a block whose refcount drops to
+ * zero goes to the back; free releases a sequence's blocks in logical order;
+ * an append takes a new block when the sequence's fill is a multiple of
+ * block_size, and on its first token copies the last block when that block is
+ * partly filled and held by another sequence (the appending sequence copies;
+ * the last holder writes in place).  Appends are all-or-nothing.
+ */
+typedef struct pa_pool pa_pool;
+
+pa_status pa_pool_create(int num_blocks, int block_size, const int32_t* free_order,
+                         pa_pool** out);
+void pa_pool_destroy(pa_pool* pool);
+
+/* New empty sequence.  PA_ERR_INVALID if seq_id exists. */
+pa_status pa_seq_create(pa_pool* pool, int64_t seq_id);
+
+/* child maps every block of parent (refcount + 1 each) and copies its fill.
+ * PA_ERR_UNKNOWN_SEQ if parent is unknown, PA_ERR_INVALID if child exists. */
+pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t child);
+
+/*
+ * Append num_tokens positions to seq.  slots_out [num_tokens] receives the
+ * slot of each new position; pairs_out [1][2] receives at most one
+ * {src, dst} copy-on-write pair, *num_pairs_out its count.  The caller must
+ * run pa_copy_blocks on the pairs before writing into the returned slots.
+ * PA_ERR_NO_BLOCKS leaves the pool unchanged.
+ */
+pa_status pa_seq_append(pa_pool* pool, int64_t seq, int num_tokens, int64_t* slots_out,
+                        int32_t* pairs_out, int* num_pairs_out);
+
+/*
+ * Append tokens_each positions to each of seqs[0..n) in that order (ids must be
+ * distinct).  slots_out [n][tokens_each]; pairs_out [n][2] (at most one pair
+ * per sequence).  All-or-nothing over the whole batch.
+ */
+pa_status pa_seq_append_batch(pa_pool* pool, const int64_t* seqs, int n, int tokens_each,
+                              int64_t* slots_out, int32_t* pairs_out, int* num_pairs_out);
+
+/* Release every block of seq in logical order and forget seq. */
+pa_status pa_seq_free(pa_pool* pool, int64_t seq);
+
+/* Copy seq's block table into out[0..cap); *num_blocks_out, *num_tokens_out get
+ * its length and fill.  PA_ERR_INVALID if cap is too small (nothing copied). */
+pa_status pa_seq_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int cap,
+                             int* num_blocks_out, int* num_tokens_out);
+
+/* Dense tables for a batch: out [n][maxb] padded with -1, lens_out [n]. */
+pa_status pa_pool_block_tables(const pa_pool* pool, const int64_t* seqs, int n, int32_t* out,
+                               int maxb, int32_t* lens_out);
+
+/* Refcount of a physical block, or -1 if out of range. */
+int pa_pool_refcount(const pa_pool* pool, int32_t block);
+
+/* Current free list, front first: out[0..cap), *n_out = its length. */
+pa_status pa_pool_free_list(const pa_pool* pool, int32_t* out, int cap, int* n_out);
+
+/* stats_out[5] = {free blocks, used blocks, shared blocks (refcount > 1),
+ * tokens held by live sequences, copy-on-write pairs issued so far}. */
+pa_status pa_pool_stats(const pa_pool* pool, int64_t* stats_out);
+
+/*
+ * Per-token KV bytes: 2 (K and V) x layers x KV heads x head_dim x element
+ * bytes (encyclopedia entry, "o problema": the OPT-13B case; briefia.fr,
+ * section "L'ampleur du cache KV": the factors).  0 for a bad dtype.
+ */
+size_t pa_kv_bytes_per_token(int num_layers, int num_kv_heads, int head_dim, int dtype);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

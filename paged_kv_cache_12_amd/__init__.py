@@ -1,0 +1,303 @@
+"""Python binding of libpa.so (PagedAttention decode for MI355X / gfx950).
+
+Argument marshalling only: every step of the decode path runs in libpa.so's
+HIP kernels or its C++ host pool.  Device arrays are torch tensors on the GPU
+(torch is used for device memory and streams); host arrays are numpy arrays.
+The functions keep the C names: pa_write_kv, pa_copy_blocks, pa_decode,
+pa_decode_workspace_size, and the pool wrapper `Pool` over pa_pool_* /
+pa_seq_*.  If libpa.so is missing every call raises; there is no fallback.
+
+Cache tensors have the library layout (x = 16 / element bytes):
+  K [num_blocks][H_kv][head_dim/x][block_size][x]
+  V [num_blocks][H_kv][block_size/x][head_dim][x]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libpa.so")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_UNKNOWN_SEQ, PA_ERR_HIP = range(6)
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
+
+# name -> (restype, argtypes), mirroring include/pa.h
+_c = ctypes
+_vp, _i, _i64, _f, _sz = _c.c_void_p, _c.c_int, _c.c_int64, _c.c_float, _c.c_size_t
+SIGNATURES = {
+    "pa_status_str": (_c.c_char_p, [_i]),
+    "pa_abi_version": (_i, []),
+    "pa_write_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "pa_copy_blocks": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "pa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "pa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i,
+                       _vp, _sz, _i, _vp]),
+    "pa_pool_create": (_i, [_i, _i, _vp, _c.POINTER(_vp)]),
+    "pa_pool_destroy": (None, [_vp]),
+    "pa_seq_create": (_i, [_vp, _i64]),
+    "pa_seq_fork": (_i, [_vp, _i64, _i64]),
+    "pa_seq_append": (_i, [_vp, _i64, _i, _vp, _vp, _vp]),
+    "pa_seq_append_batch": (_i, [_vp, _vp, _i, _i, _vp, _vp, _vp]),
+    "pa_seq_free": (_i, [_vp, _i64]),
+    "pa_seq_block_table": (_i, [_vp, _i64, _vp, _i, _vp, _vp]),
+    "pa_pool_block_tables": (_i, [_vp, _vp, _i, _vp, _i, _vp]),
+    "pa_pool_refcount": (_i, [_vp, _c.c_int32]),
+    "pa_pool_free_list": (_i, [_vp, _vp, _i, _vp]),
+    "pa_pool_stats": (_i, [_vp, _vp]),
+    "pa_kv_bytes_per_token": (_sz, [_i, _i, _i, _i]),
+}
+
+_lib = None
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_str(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_cache_12_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    try:
+        return lib().pa_status_str(status).decode()
+    except Exception:
+        return "?"
+
+
+def _check(status: int, what: str):
+    if status != PA_OK:
+        raise PAError(status, what)
+
+
+# ----------------------------------------------------------------------------
+# torch marshalling helpers
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def torch_dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _dev_ptr(t, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_ptr(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def cache_geometry(k_cache, v_cache):
+    """(num_blocks, H_kv, block_size, head_dim) from cache tensors."""
+    if k_cache.dim() != 5 or v_cache.dim() != 5:
+        raise ValueError("cache tensors must be 5-d (library layout)")
+    nb, H, dx, bs, x = k_cache.shape
+    nb2, H2, bx, d, x2 = v_cache.shape
+    if (nb, H, x) != (nb2, H2, x2) or dx * x != d or bx * x != bs:
+        raise ValueError("K and V cache shapes disagree")
+    if k_cache.dtype != v_cache.dtype or k_cache.element_size() * x != 16:
+        raise ValueError("cache dtype / vector width mismatch")
+    return nb, H, bs, d
+
+
+# ----------------------------------------------------------------------------
+# device operations
+# ----------------------------------------------------------------------------
+
+def pa_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
+    """k_new, v_new [T][H_kv][d]; slot_mapping int64 [T] (GPU tensors)."""
+    torch = _torch()
+    nb, H, bs, d = cache_geometry(k_cache, v_cache)
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    T = slot_mapping.numel()
+    if k_new.shape != (T, H, d) or v_new.shape != (T, H, d):
+        raise ValueError("k_new / v_new shape mismatch")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise TypeError("dtype mismatch")
+    st = lib().pa_write_kv(_dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
+                           _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                           _dev_ptr(slot_mapping, "slot_mapping"), T, nb, H, d, bs,
+                           torch_dtype_code(k_cache), _stream_ptr(stream))
+    _check(st, "pa_write_kv")
+
+
+def pa_copy_blocks(k_cache, v_cache, pairs, stream=None):
+    """pairs: int32 GPU tensor [P][2] of (src, dst)."""
+    torch = _torch()
+    nb, H, bs, d = cache_geometry(k_cache, v_cache)
+    if pairs.dtype != torch.int32:
+        raise TypeError("pairs must be int32")
+    P = pairs.numel() // 2
+    if P == 0:
+        return
+    st = lib().pa_copy_blocks(_dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                              _dev_ptr(pairs, "pairs"), P, nb, H, d, bs,
+                              torch_dtype_code(k_cache), _stream_ptr(stream))
+    _check(st, "pa_copy_blocks")
+
+
+def pa_decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int,
+                             max_context_len: int, partition_size: int) -> int:
+    return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim,
+                                              max_context_len, partition_size))
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+              scale: float, partition_size: int = 512, workspace=None, stream=None):
+    """out, q [B][H_q][d]; block_tables int32 [B][maxb]; context_lens int32 [B]."""
+    torch = _torch()
+    nb, H_kv, bs, d = cache_geometry(k_cache, v_cache)
+    B, H_q, dq = q.shape
+    if dq != d or out.shape != q.shape:
+        raise ValueError("q / out shape mismatch")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables / context_lens shape mismatch")
+    need = pa_decode_workspace_size(B, H_q, d, max_context_len, partition_size)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError("workspace too small")
+        ws_ptr, ws_bytes = _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    st = lib().pa_decode(_dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
+                         _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables"),
+                         block_tables.shape[1], _dev_ptr(context_lens, "context_lens"), B,
+                         max_context_len, H_q, H_kv, d, bs, nb, float(scale), partition_size,
+                         ws_ptr, ws_bytes, torch_dtype_code(q), _stream_ptr(stream))
+    _check(st, "pa_decode")
+    return workspace
+
+
+def pa_kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, dtype: int) -> int:
+    return int(lib().pa_kv_bytes_per_token(num_layers, num_kv_heads, head_dim, dtype))
+
+
+# ----------------------------------------------------------------------------
+# host block pool
+# ----------------------------------------------------------------------------
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Pool:
+    """Owner of a pa_pool (host block pool)."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        h = ctypes.c_void_p()
+        fo = None
+        if free_order is not None:
+            fo = np.ascontiguousarray(free_order, dtype=np.int32)
+            if fo.size != num_blocks:
+                raise ValueError("free_order must have num_blocks entries")
+        _check(lib().pa_pool_create(num_blocks, block_size, None if fo is None else _np_ptr(fo),
+                                    ctypes.byref(h)), "pa_pool_create")
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().pa_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def create(self, seq: int) -> int:
+        return lib().pa_seq_create(self._h, seq)
+
+    def fork(self, parent: int, child: int) -> int:
+        return lib().pa_seq_fork(self._h, parent, child)
+
+    def free(self, seq: int) -> int:
+        return lib().pa_seq_free(self._h, seq)
+
+    def append(self, seq: int, k: int):
+        """-> (status, slots int64[k], pairs int32[n][2])."""
+        return self.append_batch(np.array([seq], dtype=np.int64), k)
+
+    def append_batch(self, seqs, k: int, slots_out=None):
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = seqs.size
+        slots = slots_out if slots_out is not None else np.empty(max(1, n * k), dtype=np.int64)
+        pairs = np.empty((max(1, n), 2), dtype=np.int32)
+        npairs = ctypes.c_int(0)
+        st = lib().pa_seq_append_batch(self._h, _np_ptr(seqs), n, k, _np_ptr(slots),
+                                       _np_ptr(pairs), ctypes.byref(npairs))
+        if st != PA_OK:
+            return st, slots[:0], pairs[:0]
+        return st, slots[:n * k], pairs[:npairs.value]
+
+    def block_table(self, seq: int):
+        nb, nt = ctypes.c_int(0), ctypes.c_int(0)
+        st = lib().pa_seq_block_table(self._h, seq, None, 0, ctypes.byref(nb), ctypes.byref(nt))
+        if st == PA_ERR_UNKNOWN_SEQ:
+            raise KeyError(seq)
+        out = np.empty(max(1, nb.value), dtype=np.int32)
+        _check(lib().pa_seq_block_table(self._h, seq, _np_ptr(out), out.size, ctypes.byref(nb),
+                                        ctypes.byref(nt)), "pa_seq_block_table")
+        return out[:nb.value], nt.value
+
+    def block_tables(self, seqs, maxb: int, out=None, lens_out=None):
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = seqs.size
+        out = out if out is not None else np.empty((n, maxb), dtype=np.int32)
+        lens = lens_out if lens_out is not None else np.empty(n, dtype=np.int32)
+        _check(lib().pa_pool_block_tables(self._h, _np_ptr(seqs), n, _np_ptr(out), maxb,
+                                          _np_ptr(lens)), "pa_pool_block_tables")
+        return out, lens
+
+    def refcount(self, block: int) -> int:
+        return lib().pa_pool_refcount(self._h, block)
+
+    def free_list(self):
+        n = ctypes.c_int(0)
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        _check(lib().pa_pool_free_list(self._h, _np_ptr(out), out.size, ctypes.byref(n)),
+               "pa_pool_free_list")
+        return out[:n.value]
+
+    def stats(self):
+        s = np.zeros(5, dtype=np.int64)
+        _check(lib().pa_pool_stats(self._h, _np_ptr(s)), "pa_pool_stats")
+        return dict(zip(("free", "used", "shared", "tokens", "copies"), s.tolist()))

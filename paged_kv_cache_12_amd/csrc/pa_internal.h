@@ -1,0 +1,36 @@
+// Internal helpers shared by the HIP translation units of libpa.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/pa.h"
+
+#define PA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace pa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+inline int elem_bytes(int dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_F16:
+    case PA_BF16: return 2;
+    default: return 0;
+  }
+}
+
+inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
+inline bool supported_block_size(int bs) { return bs == 16 || bs == 32; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline pa_status launch_status() {
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace pa

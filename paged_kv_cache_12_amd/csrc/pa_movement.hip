@@ -1,0 +1,129 @@
+// Block write (pa_write_kv) and batched block copy (pa_copy_blocks) — the
+// first and third of the three custom kernels named in the vLLM encyclopedia
+// entry (tonho.wtf), section "o que isso custou".  Pure data movement: element
+// bits are moved, never converted.
+#include "pa_internal.h"
+
+namespace pa {
+
+// One thread per 16-byte vector of one (token, head): the K vector lands as a
+// single 16-byte store in the token's row of a K slab; the V vector's x
+// elements are scattered to x consecutive V slab rows (dims), position t % x.
+// E is the element storage type (uint16_t for fp16/bf16, uint32_t for fp32).
+template <typename E>
+__global__ __launch_bounds__(256) void write_kv_kernel(const E* __restrict__ k_new,
+                                                       const E* __restrict__ v_new,
+                                                       E* __restrict__ kc, E* __restrict__ vc,
+                                                       const int64_t* __restrict__ slots,
+                                                       int64_t num_tokens, int64_t num_slots,
+                                                       int H, int D, int BS) {
+  constexpr int X = 16 / sizeof(E);
+  const int nvec = D / X;
+  const int64_t total = num_tokens * H * nvec;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int jv = static_cast<int>(idx % nvec);
+    const int64_t th = idx / nvec;
+    const int h = static_cast<int>(th % H);
+    const int64_t t = th / H;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t b = slot / BS;
+    const int tt = static_cast<int>(slot - b * BS);
+    const int64_t src = (t * H + h) * D + jv * X;
+    const int64_t tile = (b * H + h) * static_cast<int64_t>(BS) * D;
+    // K(b, h, tt, i) at tile + ((i / X) * BS + tt) * X + i % X
+    *reinterpret_cast<u32x4*>(kc + tile + (static_cast<int64_t>(jv) * BS + tt) * X) =
+        *reinterpret_cast<const u32x4*>(k_new + src);
+    // V(b, h, tt, i) at tile + ((tt / X) * D + i) * X + tt % X
+    union {
+      u32x4 v;
+      E e[X];
+    } vals;
+    vals.v = *reinterpret_cast<const u32x4*>(v_new + src);
+    E* vdst = vc + tile + (static_cast<int64_t>(tt / X) * D + jv * X) * X + tt % X;
+#pragma unroll
+    for (int e = 0; e < X; ++e) vdst[e * X] = vals.e[e];
+  }
+}
+
+// grid (chunks, num_pairs, 2): z selects the K or the V cache; each thread
+// copies 16-byte vectors of one block.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ kc,
+                                                          u32x4* __restrict__ vc,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int num_blocks, int64_t vecs_per_block) {
+  const int pi = blockIdx.y;
+  const int32_t src = pairs[2 * pi];
+  const int32_t dst = pairs[2 * pi + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+  u32x4* base = blockIdx.z ? vc : kc;
+  const u32x4* from = base + src * vecs_per_block;
+  u32x4* to = base + dst * vecs_per_block;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < vecs_per_block;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    to[i] = from[i];
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+PA_EXPORT pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, const int64_t* slot_mapping, int num_tokens,
+                                int num_blocks, int num_kv_heads, int head_dim, int block_size,
+                                int dtype, void* stream) {
+  const int e = elem_bytes(dtype);
+  if (e == 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PA_ERR_INVALID;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t nvec = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim * e / 16);
+  const int threads = 256;
+  const int64_t want = (nvec + threads - 1) / threads;
+  const int blocks = static_cast<int>(want < 65536 ? want : 65536);
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  if (e == 2) {
+    hipLaunchKernelGGL(write_kv_kernel<uint16_t>, dim3(blocks), dim3(threads), 0, st,
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                       slot_mapping, static_cast<int64_t>(num_tokens), num_slots, num_kv_heads,
+                       head_dim, block_size);
+  } else {
+    hipLaunchKernelGGL(write_kv_kernel<uint32_t>, dim3(blocks), dim3(threads), 0, st,
+                       static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new),
+                       static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
+                       slot_mapping, static_cast<int64_t>(num_tokens), num_slots, num_kv_heads,
+                       head_dim, block_size);
+  }
+  return launch_status();
+}
+
+PA_EXPORT pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
+                                   int num_pairs, int num_blocks, int num_kv_heads, int head_dim,
+                                   int block_size, int dtype, void* stream) {
+  const int e = elem_bytes(dtype);
+  if (e == 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PA_ERR_INVALID;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !pairs) return PA_ERR_INVALID;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID;
+  if (num_pairs > 65535) return PA_ERR_INVALID;
+  const int64_t vecs = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * e / 16;
+  const int threads = 256;
+  int64_t chunks = (vecs + threads * 4 - 1) / (threads * 4);
+  if (chunks < 1) chunks = 1;
+  if (chunks > 1024) chunks = 1024;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<unsigned>(chunks), num_pairs, 2),
+                     dim3(threads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), pairs,
+                     num_blocks, vecs);
+  return launch_status();
+}

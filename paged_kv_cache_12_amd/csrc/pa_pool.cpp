@@ -1,0 +1,295 @@
+// Host-side KV block pool: per-sequence block tables, refcounts, fork / append /
+// free and copy-on-write decisions (vLLM encyclopedia entry, tonho.wtf, section
+// "como funciona").  Host memory only; no HIP calls.
+//
+// The free list is a ring buffer holding each free block id once (FIFO: take
+// from the front, return to the back).  Sequences live in a hash map keyed by
+// the caller's 64-bit id.  Every operation is O(tokens + blocks touched).
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/pa.h"
+
+#define PA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+struct Seq {
+  std::vector<int32_t> table;
+  int64_t fill = 0;
+};
+
+}  // namespace
+
+struct pa_pool {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> ring;  // free list storage, capacity num_blocks
+  int64_t head = 0;           // index of the front element
+  int64_t count = 0;          // number of free blocks
+  std::vector<int32_t> ref;
+  std::unordered_map<int64_t, Seq> seqs;
+  int64_t copies = 0;
+  int64_t tokens = 0;
+
+  int32_t alloc() {
+    int32_t b = ring[head];
+    head = (head + 1) % num_blocks;
+    --count;
+    ref[b] = 1;
+    return b;
+  }
+  void release(int32_t b) {
+    if (--ref[b] == 0) {
+      ring[(head + count) % num_blocks] = b;
+      ++count;
+    }
+  }
+};
+
+namespace {
+
+// Blocks that appending k tokens to `s` takes, when the refcount of its last
+// block is `last_ref`.
+int64_t blocks_needed(const Seq& s, int64_t k, int32_t bs, int32_t last_ref) {
+  if (k <= 0) return 0;
+  const int64_t n = s.fill;
+  // positions n .. n+k-1 that start a block
+  int64_t need = (n + k + bs - 1) / bs - (n + bs - 1) / bs;
+  if (n % bs != 0 && last_ref > 1) need += 1;
+  return need;
+}
+
+void append_one(pa_pool* p, Seq& s, int64_t k, int64_t* slots, int32_t* pair, int* npairs) {
+  const int32_t bs = p->block_size;
+  for (int64_t j = 0; j < k; ++j) {
+    const int64_t n = s.fill;
+    if (n % bs == 0) {
+      s.table.push_back(p->alloc());
+    } else if (j == 0 && p->ref[s.table.back()] > 1) {
+      const int32_t old = s.table.back();
+      const int32_t nb = p->alloc();
+      pair[0] = old;
+      pair[1] = nb;
+      ++*npairs;
+      ++p->copies;
+      p->release(old);
+      s.table.back() = nb;
+    }
+    slots[j] = static_cast<int64_t>(s.table.back()) * bs + n % bs;
+    s.fill = n + 1;
+  }
+  p->tokens += k;
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_pool_create(int num_blocks, int block_size, const int32_t* free_order,
+                                   pa_pool** out) {
+  if (!out || num_blocks <= 0 || block_size <= 0) return PA_ERR_INVALID;
+  *out = nullptr;
+  pa_pool* p = new (std::nothrow) pa_pool();
+  if (!p) return PA_ERR_INVALID;
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->ring.resize(num_blocks);
+  p->ref.assign(num_blocks, 0);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int i = 0; i < num_blocks; ++i) {
+      const int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete p;
+        return PA_ERR_INVALID;
+      }
+      seen[b] = 1;
+      p->ring[i] = b;
+    }
+  } else {
+    for (int i = 0; i < num_blocks; ++i) p->ring[i] = i;
+  }
+  p->head = 0;
+  p->count = num_blocks;
+  *out = p;
+  return PA_OK;
+}
+
+PA_EXPORT void pa_pool_destroy(pa_pool* pool) { delete pool; }
+
+PA_EXPORT pa_status pa_seq_create(pa_pool* p, int64_t seq_id) {
+  if (!p) return PA_ERR_INVALID;
+  if (p->seqs.count(seq_id)) return PA_ERR_INVALID;
+  p->seqs.emplace(seq_id, Seq());
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_seq_fork(pa_pool* p, int64_t parent, int64_t child) {
+  if (!p) return PA_ERR_INVALID;
+  auto it = p->seqs.find(parent);
+  if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+  if (p->seqs.count(child)) return PA_ERR_INVALID;
+  Seq c = it->second;  // copy before emplace (rehash may move it)
+  for (int32_t b : c.table) ++p->ref[b];
+  p->tokens += c.fill;
+  p->seqs.emplace(child, std::move(c));
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_seq_append_batch(pa_pool* p, const int64_t* seqs, int n, int tokens_each,
+                                        int64_t* slots_out, int32_t* pairs_out,
+                                        int* num_pairs_out) {
+  if (!p || n < 0 || tokens_each < 0) return PA_ERR_INVALID;
+  if (n > 0 && !seqs) return PA_ERR_INVALID;
+  if (n > 0 && tokens_each > 0 && (!slots_out || !pairs_out)) return PA_ERR_INVALID;
+  if (num_pairs_out) *num_pairs_out = 0;
+  // resolve ids, reject duplicates
+  std::vector<Seq*> ss(n);
+  for (int i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+    ss[i] = &it->second;
+  }
+  {
+    std::vector<int64_t> ids(seqs, seqs + n);
+    std::sort(ids.begin(), ids.end());
+    if (std::adjacent_find(ids.begin(), ids.end()) != ids.end()) return PA_ERR_INVALID;
+  }
+  if (tokens_each == 0 || n == 0) return PA_OK;
+  // dry run: blocks the whole batch takes, tracking refcount drops of copied blocks
+  const int32_t bs = p->block_size;
+  std::unordered_map<int32_t, int32_t> overlay;
+  int64_t need = 0;
+  for (int i = 0; i < n; ++i) {
+    const Seq& s = *ss[i];
+    int32_t last_ref = 0;
+    int32_t last = -1;
+    if (!s.table.empty()) {
+      last = s.table.back();
+      auto o = overlay.find(last);
+      last_ref = (o == overlay.end()) ? p->ref[last] : o->second;
+    }
+    need += blocks_needed(s, tokens_each, bs, last_ref);
+    if (s.fill % bs != 0 && last_ref > 1) overlay[last] = last_ref - 1;
+  }
+  if (need > p->count) return PA_ERR_NO_BLOCKS;
+  int np = 0;
+  for (int i = 0; i < n; ++i) {
+    int got = 0;
+    append_one(p, *ss[i], tokens_each, slots_out + static_cast<int64_t>(i) * tokens_each,
+               pairs_out + 2 * np, &got);
+    np += got;
+  }
+  if (num_pairs_out) *num_pairs_out = np;
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_seq_append(pa_pool* p, int64_t seq, int num_tokens, int64_t* slots_out,
+                                  int32_t* pairs_out, int* num_pairs_out) {
+  return pa_seq_append_batch(p, &seq, 1, num_tokens, slots_out, pairs_out, num_pairs_out);
+}
+
+PA_EXPORT pa_status pa_seq_free(pa_pool* p, int64_t seq) {
+  if (!p) return PA_ERR_INVALID;
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+  for (int32_t b : it->second.table) p->release(b);
+  p->tokens -= it->second.fill;
+  p->seqs.erase(it);
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_seq_block_table(const pa_pool* p, int64_t seq, int32_t* out, int cap,
+                                       int* num_blocks_out, int* num_tokens_out) {
+  if (!p || cap < 0) return PA_ERR_INVALID;
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+  const Seq& s = it->second;
+  const int64_t nb = static_cast<int64_t>(s.table.size());
+  if (num_blocks_out) *num_blocks_out = static_cast<int>(nb);
+  if (num_tokens_out) *num_tokens_out = static_cast<int>(s.fill);
+  if (nb > cap) return PA_ERR_INVALID;
+  if (nb && !out) return PA_ERR_INVALID;
+  if (nb) std::memcpy(out, s.table.data(), nb * sizeof(int32_t));
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_pool_block_tables(const pa_pool* p, const int64_t* seqs, int n,
+                                         int32_t* out, int maxb, int32_t* lens_out) {
+  if (!p || n < 0 || maxb < 0) return PA_ERR_INVALID;
+  if (n > 0 && (!seqs || !out || !lens_out)) return PA_ERR_INVALID;
+  std::vector<const Seq*> ss(n);
+  for (int i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+    if (static_cast<int64_t>(it->second.table.size()) > maxb) return PA_ERR_INVALID;
+    ss[i] = &it->second;
+  }
+  for (int i = 0; i < n; ++i) {
+    int32_t* row = out + static_cast<int64_t>(i) * maxb;
+    const auto& t = ss[i]->table;
+    std::copy(t.begin(), t.end(), row);
+    std::fill(row + t.size(), row + maxb, -1);
+    lens_out[i] = static_cast<int32_t>(ss[i]->fill);
+  }
+  return PA_OK;
+}
+
+PA_EXPORT int pa_pool_refcount(const pa_pool* p, int32_t block) {
+  if (!p || block < 0 || block >= p->num_blocks) return -1;
+  return p->ref[block];
+}
+
+PA_EXPORT pa_status pa_pool_free_list(const pa_pool* p, int32_t* out, int cap, int* n_out) {
+  if (!p || cap < 0) return PA_ERR_INVALID;
+  if (n_out) *n_out = static_cast<int>(p->count);
+  if (p->count > cap) return PA_ERR_INVALID;
+  if (p->count && !out) return PA_ERR_INVALID;
+  for (int64_t i = 0; i < p->count; ++i) out[i] = p->ring[(p->head + i) % p->num_blocks];
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_pool_stats(const pa_pool* p, int64_t* stats_out) {
+  if (!p || !stats_out) return PA_ERR_INVALID;
+  int64_t used = 0, shared = 0;
+  for (int32_t r : p->ref) {
+    used += r > 0;
+    shared += r > 1;
+  }
+  stats_out[0] = p->count;
+  stats_out[1] = used;
+  stats_out[2] = shared;
+  stats_out[3] = p->tokens;
+  stats_out[4] = p->copies;
+  return PA_OK;
+}
+
+PA_EXPORT size_t pa_kv_bytes_per_token(int num_layers, int num_kv_heads, int head_dim,
+                                       int dtype) {
+  size_t e;
+  switch (dtype) {
+    case PA_F32: e = 4; break;
+    case PA_F16:
+    case PA_BF16: e = 2; break;
+    default: return 0;
+  }
+  if (num_layers < 0 || num_kv_heads < 0 || head_dim < 0) return 0;
+  return 2 * static_cast<size_t>(num_layers) * num_kv_heads * head_dim * e;
+}
+
+PA_EXPORT const char* pa_status_str(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PA_ERR_NO_BLOCKS: return "not enough free blocks";
+    case PA_ERR_UNKNOWN_SEQ: return "unknown sequence id";
+    case PA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+PA_EXPORT int pa_abi_version(void) { return 1; }

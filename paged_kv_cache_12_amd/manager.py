@@ -1,0 +1,129 @@
+"""Central KV-cache manager: one host block pool plus the device caches.
+
+The vLLM encyclopedia entry (tonho.wtf), section "como funciona", has a single
+central KV-cache manager that hands the block tables to the workers together
+with each iteration's input.  PagedKVCache is that manager for one GPU: the C++
+pool decides slots and copy-on-write pairs, and the device operations
+(pa_copy_blocks, pa_write_kv, pa_decode) run on the caller's stream.  Metadata
+goes to the device through pinned host buffers with asynchronous copies.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import (Pool, PA_OK, PAError, pa_copy_blocks, pa_decode, pa_decode_workspace_size,
+               pa_write_kv)
+
+TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+
+
+def storage_to_torch(a: np.ndarray, dtype: str):
+    """Host storage array (bf16 as uint16 bits) -> CPU torch tensor of dtype."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    return torch.from_numpy(a)
+
+
+def torch_to_storage(t, dtype: str) -> np.ndarray:
+    """CPU/GPU torch tensor -> host storage array (bf16 as uint16 bits)."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class PagedKVCache:
+    """Device K/V caches in the library layout plus the host pool.
+
+    guard_blocks extra blocks are allocated before and after the pool proper
+    (never handed out) so that tests can check nothing writes outside it.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+                 dtype: str, device="cuda", free_order=None, guard_blocks: int = 0,
+                 fill_bits: int | None = None):
+        import torch
+        self.torch = torch
+        self.dtype = dtype
+        self.tdtype = getattr(torch, TORCH_DTYPES[dtype])
+        self.num_blocks, self.bs, self.H, self.d = num_blocks, block_size, num_kv_heads, head_dim
+        esz = 4 if dtype == "f32" else 2
+        self.x = 16 // esz
+        self.guard = guard_blocks
+        tot = num_blocks + 2 * guard_blocks
+        kshape = (tot, num_kv_heads, head_dim // self.x, block_size, self.x)
+        vshape = (tot, num_kv_heads, block_size // self.x, head_dim, self.x)
+        self.k_full = torch.empty(kshape, dtype=self.tdtype, device=device)
+        self.v_full = torch.empty(vshape, dtype=self.tdtype, device=device)
+        if fill_bits is not None:
+            ib = torch.int32 if esz == 4 else torch.int16
+            val = fill_bits if fill_bits < (1 << (8 * esz - 1)) else fill_bits - (1 << (8 * esz))
+            self.k_full.view(ib).fill_(val)
+            self.v_full.view(ib).fill_(val)
+        self.k_cache = self.k_full[guard_blocks:guard_blocks + num_blocks]
+        self.v_cache = self.v_full[guard_blocks:guard_blocks + num_blocks]
+        self.pool = Pool(num_blocks, block_size, free_order)
+        self.device = device
+        self._ws = None
+
+    # -- pool operations ----------------------------------------------------
+    def create(self, seq: int):
+        st = self.pool.create(seq)
+        if st != PA_OK:
+            raise PAError(st, "pa_seq_create")
+
+    def fork(self, parent: int, child: int):
+        st = self.pool.fork(parent, child)
+        if st != PA_OK:
+            raise PAError(st, "pa_seq_fork")
+
+    def free(self, seq: int):
+        st = self.pool.free(seq)
+        if st != PA_OK:
+            raise PAError(st, "pa_seq_free")
+
+    # -- append: pool slots, copy-on-write, block write ----------------------
+    def append(self, seqs, k: int, k_new, v_new, stream=None):
+        """Append k tokens to each sequence in `seqs` (in order).  k_new, v_new:
+        GPU tensors [len(seqs)*k][H][d] in the same order.  Runs pa_copy_blocks
+        for any copy-on-write pair before pa_write_kv.  Returns (slots, pairs)."""
+        torch = self.torch
+        st, slots, pairs = self.pool.append_batch(seqs, k)
+        if st != PA_OK:
+            raise PAError(st, "pa_seq_append_batch")
+        if len(pairs):
+            dp = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device)
+            pa_copy_blocks(self.k_cache, self.v_cache, dp, stream=stream)
+        if len(slots):
+            ds = torch.from_numpy(np.ascontiguousarray(slots)).to(self.device)
+            pa_write_kv(k_new, v_new, self.k_cache, self.v_cache, ds, stream=stream)
+        return slots, pairs
+
+    # -- decode ---------------------------------------------------------------
+    def tables(self, seqs, maxb: int | None = None):
+        """Host block tables [n][maxb] (-1 padded) and context lengths."""
+        seqs = np.asarray(seqs, dtype=np.int64)
+        if maxb is None:
+            maxb = 1
+            for s in seqs:
+                t, _ = self.pool.block_table(int(s))
+                maxb = max(maxb, len(t))
+        return self.pool.block_tables(seqs, maxb)
+
+    def decode(self, q, seqs, scale: float, partition_size: int = 512, out=None, stream=None):
+        torch = self.torch
+        tables, lens = self.tables(seqs)
+        max_ctx = int(lens.max()) if lens.size else 0
+        bt = torch.from_numpy(tables).to(self.device)
+        ln = torch.from_numpy(lens).to(self.device)
+        if out is None:
+            out = torch.empty_like(q)
+        need = pa_decode_workspace_size(q.shape[0], q.shape[1], self.d, max_ctx, partition_size)
+        if need and (self._ws is None or self._ws.numel() < need):
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        pa_decode(out, q, self.k_cache, self.v_cache, bt, ln, max_ctx, scale, partition_size,
+                  workspace=self._ws if need else None, stream=stream)
+        return out, tables, lens
