@@ -36,12 +36,16 @@
  * x = 16 / element_bytes (8 for fp16 and bf16, 4 for fp32), one (block, head)
  * tile is block_size * head_dim contiguous elements, and
  *   K cache [num_blocks][H_kv][head_dim/x][block_size][x]
- *       K(block b, head h, token t, dim i) at [b][h][i/x][t][i%x]
+ *       K(block b, head h, token t, dim i) at [b][h][i/x][r(t)][i%x]
+ *       r(t) = (t & 4 ? block_size/2 : 0) + 4*(t >> 3) + (t & 3): inside each
+ *       slab the tokens whose index has bit 2 clear come first, in order,
+ *       then those with bit 2 set
  *   V cache [num_blocks][H_kv][block_size/x][head_dim][x]
  *       V(block b, head h, token t, dim i) at [b][h][t/x][i][t%x]
  * Both are built from 16-byte vectors: a K vector holds x consecutive dims of
  * one token, a V vector holds x consecutive tokens of one dim, which are the
- * operand shapes of the decode kernel's QK and PV matrix products.
+ * operand shapes of the decode kernel's QK and PV matrix products; the K row
+ * order makes each QK operand load read whole 128-byte lines.
  *
  * Slot: slot = physical_block * block_size + offset_in_block.
  */
@@ -135,7 +139,7 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  *   partition_size  0: one work unit per (sequence, KV head); otherwise the
  *        context is split into partitions of this many tokens (a multiple of
  *        32) whose partial results (running max, sum, unnormalised output)
- *        are merged by a log-sum-exp reduce in ascending partition order
+ *        are merged by a log-sum-exp reduce in a fixed order
  *   workspace  device, >= pa_decode_workspace_size(...) bytes (may be NULL
  *        when that is 0); contents on entry are ignored
  *

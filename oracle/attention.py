@@ -23,7 +23,9 @@ Readings where the pages are silent:
 Cache layout (the library's ABI; the pages do not fix one).  With
 x = 16 / element_bytes (8 for fp16/bf16, 4 for fp32):
   K cache [num_blocks][H_kv][head_dim/x][block_size][x]:
-      element (block b, head h, token-in-block t, dim i) at [b][h][i//x][t][i%x]
+      element (block b, head h, token-in-block t, dim i) at
+      [b][h][i//x][k_row(t)][i%x], where k_row stores the tokens whose index
+      has bit 2 clear first (in increasing order), then those with bit 2 set
   V cache [num_blocks][H_kv][block_size/x][head_dim][x]:
       element (b, h, t, i) at [b][h][t//x][i][t%x]
 """
@@ -54,9 +56,14 @@ def to_f64(raw: np.ndarray, dtype: str) -> np.ndarray:
 # Cache layout: explicit per-element offsets, and whole-array views.
 # ----------------------------------------------------------------------------
 
+def k_row(t, bs):
+    """Row of token t inside a K slab: tokens with bit 2 clear, then set."""
+    return (bs // 2 if t & 4 else 0) + 4 * (t >> 3) + (t & 3)
+
+
 def k_offset(b, h, t, i, H, bs, d, x):
     """Flat element offset of K(block b, head h, token t, dim i)."""
-    return (((b * H + h) * (d // x) + i // x) * bs + t) * x + i % x
+    return (((b * H + h) * (d // x) + i // x) * bs + k_row(t, bs)) * x + i % x
 
 
 def v_offset(b, h, t, i, H, bs, d, x):
@@ -74,10 +81,15 @@ def v_cache_shape(num_blocks, H, bs, d, dtype):
     return (num_blocks, H, bs // x, d, x)
 
 
+def _k_rows(bs):
+    return np.array([k_row(t, bs) for t in range(bs)], dtype=np.int64)
+
+
 def _k_tokens(kblocks: np.ndarray) -> np.ndarray:
-    """[n][H][d/x][bs][x] -> [n*bs][H][d] in logical token order."""
+    """[n][H][d/x][bs rows][x] -> [n*bs][H][d] in logical token order."""
     n, H, dx, bs, x = kblocks.shape
-    return kblocks.transpose(0, 3, 1, 2, 4).reshape(n * bs, H, dx * x)
+    by_token = kblocks[:, :, :, _k_rows(bs), :]
+    return by_token.transpose(0, 3, 1, 2, 4).reshape(n * bs, H, dx * x)
 
 
 def _v_tokens(vblocks: np.ndarray) -> np.ndarray:
@@ -192,8 +204,8 @@ def write_kv(k_cache, v_cache, k_new, v_new, slots):
     vn = np.asarray(v_new)[keep]
     T = kn.shape[0]
     d = kn.shape[2]
-    # K: [b][h][i//x][t][i%x] <- kn[j][h][i]
-    k_cache[b, :, :, t, :] = kn.reshape(T, H, d // x, x)
+    # K: [b][h][i//x][k_row(t)][i%x] <- kn[j][h][i]
+    k_cache[b, :, :, _k_rows(bs)[t], :] = kn.reshape(T, H, d // x, x)
     # V: [b][h][t//x][i][t%x] <- vn[j][h][i]
     v_cache[b, :, t // x, :, t % x] = vn
 

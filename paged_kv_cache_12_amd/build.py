@@ -33,10 +33,11 @@ def _compile(src: str, obj: str, extra: list[str]) -> subprocess.Popen:
     return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compile every source and link libpa.so; returns its path."""
+def build(verbose: bool = False, extra: list[str] | None = None, out: str | None = None) -> str:
+    """Compile every source and link libpa.so (or `out`); returns its path."""
     extra = list(extra or [])
-    os.makedirs(LIBDIR, exist_ok=True)
+    out = out or LIB
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = tempfile.mkdtemp(prefix="pa_build_")
     try:
         procs = []
@@ -58,10 +59,10 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
         r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
         if r.returncode != 0:
             raise RuntimeError("link failed:\n" + r.stdout)
-        shutil.move(tmp_lib, LIB)
+        shutil.move(tmp_lib, out)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

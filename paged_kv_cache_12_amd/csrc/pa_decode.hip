@@ -23,7 +23,21 @@
 //   A[row c][k 8g..8g+7], B[k 8g..8g+7][col c], D[row 4g+r][col c], r = 0..3.
 #include "pa_internal.h"
 
+#ifndef PA_LAZY
+#define PA_LAZY 1
+#endif
+#ifndef PA_PIPE
+#define PA_PIPE 0
+#endif
+#ifndef PA_WAVES
+#define PA_WAVES 2
+#endif
+
 namespace pa {
+
+// Scores more than this many log2 units above the running reference trigger a
+// rescale; weights fed to the PV product are at most 2^kRescaleLog2.
+constexpr float kRescaleLog2 = 8.0f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -73,8 +87,164 @@ __device__ __forceinline__ Span partition_span(const int32_t* ctx_lens, int s, i
   return sp;
 }
 
+// Registers holding one 32-token group's operands.
+template <typename T, int D>
+struct GroupTiles {
+  typedef typename Mfma<T>::v8 v8;
+  v8 k[2][D / 32];
+  v8 v[D / 16];
+};
+
+// K/V tiles are read once per step: non-temporal loads.
+template <typename V>
+__device__ __forceinline__ V load16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+}
+
+// Row of token t inside a K slab (tokens with bit 2 clear first).
+template <int BS>
+__device__ __forceinline__ int k_row(int t) {
+  return ((t & 4) ? BS / 2 : 0) + 4 * (t >> 3) + (t & 3);
+}
+
+// Block-table window: lane i holds entry lb_base + i of the sequence's table
+// (64 entries per window, refilled when a group crosses it).  Entries past the
+// context, or out of range, read as block 0; the tokens they stand for are
+// masked, so the value only has to be a valid block.
+struct TableWindow {
+  int lb_base;
+  int ids;  // this lane's entry
+};
+
+__device__ __forceinline__ void fill_window(TableWindow& w, const int32_t* __restrict__ bt,
+                                            int lb_base, int nb_valid, int num_blocks,
+                                            int lane) {
+  w.lb_base = lb_base;
+  int b = 0;
+  if (lb_base + lane < nb_valid) b = bt[lb_base + lane];
+  if (b < 0 || b >= num_blocks) b = 0;
+  w.ids = b;
+}
+
 template <typename T, int D, int BS>
-__global__ __launch_bounds__(64) void decode_part_mfma(
+__device__ __forceinline__ void load_group(GroupTiles<T, D>& G, TableWindow& w,
+                                           const int32_t* __restrict__ bt, int tg, int nb_valid,
+                                           int num_blocks, const T* kh, const T* vh,
+                                           int64_t blk_stride, const int* kblk, const int* krow,
+                                           int vblk, int vslab, int g, int c, int lane) {
+  typedef typename Mfma<T>::v8 v8;
+  constexpr int NC = D / 32, NJ = D / 16, BPT = 32 / BS;
+  const int lb0 = tg / BS;
+  if (lb0 + BPT - 1 >= w.lb_base + 64) fill_window(w, bt, lb0, nb_valid, num_blocks, lane);
+  int pb[BPT];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) pb[j] = __builtin_amdgcn_readlane(w.ids, lb0 + j - w.lb_base);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const T* base = kh + pb[kblk[h]] * blk_stride + krow[h] * 8;
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+      G.k[h][k] = load16<v8>(base + (4 * k + g) * (BS * 8));
+  }
+  const T* base = vh + pb[vblk] * blk_stride + vslab * (D * 8) + c * 8;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) G.v[j] = load16<v8>(base + 16 * j * 8);
+}
+
+// QK, online-softmax update and PV for one 32-token group.  TAIL: only the
+// first `rem` tokens of the group are inside the context (the last group of a
+// partition); the others are masked out of the scores and their V operands
+// are zeroed, since slots past the fill may hold anything (0 * NaN = NaN).
+template <typename T, int D, bool TAIL>
+__device__ __forceinline__ void compute_group(GroupTiles<T, D>& G,
+                                              const typename Mfma<T>::v8* qop, f32x4* o,
+                                              float& m, float& l, int rem, int g,
+                                              float scale_log2) {
+  typedef Mfma<T> M;
+  typedef typename M::v8 v8;
+  constexpr int NC = D / 32, NJ = D / 16;
+  f32x4 sacc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    sacc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NC; ++k) sacc[h] = M::mma(G.k[h][k], qop[k], sacc[h]);
+  }
+  // raw scores of tokens 8g + 4h + r (scale > 0, so the max commutes with it)
+  float x[8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[4 * h + r] = sacc[h][r];
+      if (TAIL && 8 * g + 4 * h + r >= rem) x[4 * h + r] = -INFINITY;
+    }
+  float mraw = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  const float mloc = mraw * scale_log2;
+#if PA_LAZY
+  // Lazy rescale: the reference m only moves when a score exceeds it by more
+  // than kRescaleLog2, so weights stay <= 2^kRescaleLog2 and the accumulators
+  // are rescaled only on this wave-uniform, rarely taken path.
+  if (__builtin_amdgcn_ballot_w64(mloc > m + kRescaleLog2)) {
+    __asm__ volatile("");  // keep the path a real branch (not speculated)
+    float mw = xor_max(mloc, 16);
+    mw = xor_max(mw, 32);
+    const float mnew = fmaxf(m, mw);
+    const float alpha = fast_exp2(m - mnew);
+    l *= alpha;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) o[j] *= alpha;
+    m = mnew;
+  }
+  float psum = 0.f;
+  v8 pop;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float e = fast_exp2(fmaf(x[i], scale_log2, -m));
+    psum += e;
+    pop[i] = static_cast<T>(e);
+  }
+  l += psum;
+#else
+  float mw = xor_max(mloc, 16);
+  mw = xor_max(mw, 32);
+  const float mnew = fmaxf(m, mw);
+  const float alpha = fast_exp2(m - mnew);
+  float psum = 0.f;
+  v8 pop;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float e = fast_exp2(fmaf(x[i], scale_log2, -mnew));
+    psum += e;
+    pop[i] = static_cast<T>(e);
+  }
+  l = l * alpha + psum;
+  m = mnew;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) o[j] *= alpha;
+#endif
+  if (TAIL) {
+    // keep the first nv of this lane's 8 V elements (16-bit lanes of 4 dwords)
+    const int nv = rem - 8 * g;
+    u32x4 keep;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      keep[w] = (2 * w < nv ? 0x0000FFFFu : 0u) | (2 * w + 1 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      u32x4 bits = __builtin_bit_cast(u32x4, G.v[j]);
+      bits &= keep;
+      G.v[j] = __builtin_bit_cast(v8, bits);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) o[j] = M::mma(G.v[j], pop, o[j]);
+}
+
+template <typename T, int D, int BS>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES)))
+void decode_part_mfma(
     T* __restrict__ out, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ block_tables, int maxb, const int32_t* __restrict__ ctx_lens,
@@ -84,7 +254,6 @@ __global__ __launch_bounds__(64) void decode_part_mfma(
   typedef typename M::v8 v8;
   constexpr int NC = D / 32;    // QK k-chunks of 32 dims
   constexpr int NJ = D / 16;    // PV output chunks of 16 dims
-  constexpr int BPT = 32 / BS;  // blocks per 32-token group
   constexpr int TILE = BS * D;  // elements per (block, head) tile
 
   const int lane = threadIdx.x;
@@ -127,91 +296,59 @@ __global__ __launch_bounds__(64) void decode_part_mfma(
   // Token (within the 32-token group) whose K row this lane feeds to QK MFMA h:
   // row c holds token 8(c/4) + 4h + c%4, so that output lane group g, register
   // r of MFMA h is token 8g + 4h + r.
-  int ku[2], kblk[2], krow[2];
+  int kblk[2], krow[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    ku[h] = 8 * (c >> 2) + 4 * h + (c & 3);
-    kblk[h] = ku[h] / BS;
-    krow[h] = ku[h] % BS;
+    const int u = 8 * (c >> 2) + 4 * h + (c & 3);
+    kblk[h] = u / BS;
+    krow[h] = k_row<BS>(u % BS);
   }
   // V: lane group g feeds tokens 8g .. 8g+7: block vblk, slab vslab.
   const int vblk = (8 * g) / BS;
   const int vslab = ((8 * g) % BS) / 8;
 
-  for (int tg = t0; tg < t1; tg += 32) {
-    int pb[BPT];
-    const int lb0 = tg / BS;
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      int b = -1;
-      if ((lb0 + j) * BS < t1) b = bt[lb0 + j];
-      if (b < 0 || b >= num_blocks) b = (j == 0) ? 0 : pb[0];
-      pb[j] = b;
+  // Two register sets: group i+1 is loading while group i is computed.
+  // Full 32-token groups, then at most one partial group at the end.
+  const int tfull = t0 + ((t1 - t0) & ~31);
+  const int nb_valid = (t1 + BS - 1) / BS;  // table entries inside the context
+  TableWindow win;
+  fill_window(win, bt, t0 / BS, nb_valid, num_blocks, lane);
+#if PA_PIPE
+  // Two register sets: group i+1 is loading while group i is computed.
+  GroupTiles<T, D> A, B;
+  if (t0 < t1)
+    load_group<T, D, BS>(A, win, bt, t0, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
+                         vblk, vslab, g, c, lane);
+  int tg = t0;
+  while (tg < tfull) {
+    if (tg + 32 < t1)
+      load_group<T, D, BS>(B, win, bt, tg + 32, nb_valid, num_blocks, kh, vh, blk_stride, kblk,
+                           krow, vblk, vslab, g, c, lane);
+    compute_group<T, D, false>(A, qop, o, m, l, 32, g, scale_log2);
+    tg += 32;
+    if (tg >= tfull) {
+      if (tg < t1) compute_group<T, D, true>(B, qop, o, m, l, t1 - tg, g, scale_log2);
+      tg = t1;
+      break;
     }
-    v8 kr[2][NC];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const T* base = kh + pb[kblk[h]] * blk_stride + krow[h] * 8;
-#pragma unroll
-      for (int k = 0; k < NC; ++k)
-        kr[h][k] = *reinterpret_cast<const v8*>(base + (4 * k + g) * (BS * 8));
-    }
-    v8 vr[NJ];
-    {
-      const T* base = vh + pb[vblk] * blk_stride + vslab * (D * 8) + c * 8;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) vr[j] = *reinterpret_cast<const v8*>(base + 16 * j * 8);
-    }
-
-    // scores
-    f32x4 sacc[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      sacc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < NC; ++k) sacc[h] = M::mma(kr[h][k], qop[k], sacc[h]);
-    }
-    const int rem = t1 - tg;  // valid tokens in this group (>= 1)
-    float x[8];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int u = 8 * g + 4 * h + r;
-        x[4 * h + r] = (u < rem) ? sacc[h][r] * scale_log2 : -INFINITY;
-      }
-    float mloc = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mloc = fmaxf(mloc, x[i]);
-    mloc = xor_max(mloc, 16);
-    mloc = xor_max(mloc, 32);
-    const float mnew = fmaxf(m, mloc);
-    const float alpha = fast_exp2(m - mnew);
-    float psum = 0.f;
-    v8 pop;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float e = fast_exp2(x[i] - mnew);
-      psum += e;
-      pop[i] = static_cast<T>(e);
-    }
-    l = l * alpha + psum;
-    m = mnew;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) o[j] *= alpha;
-
-    if (rem < 32) {
-      // tail: positions past the context may hold anything (0 * NaN = NaN)
-      const int nv = rem - 8 * g;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (i >= nv) vr[j][i] = static_cast<T>(0.f);
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) o[j] = M::mma(vr[j], pop, o[j]);
+    if (tg + 32 < t1)
+      load_group<T, D, BS>(A, win, bt, tg + 32, nb_valid, num_blocks, kh, vh, blk_stride, kblk,
+                           krow, vblk, vslab, g, c, lane);
+    compute_group<T, D, false>(B, qop, o, m, l, 32, g, scale_log2);
+    tg += 32;
   }
+  if (tg < t1) compute_group<T, D, true>(A, qop, o, m, l, t1 - tg, g, scale_log2);
+#else
+  for (int tg = t0; tg < t1; tg += 32) {
+    GroupTiles<T, D> A;
+    load_group<T, D, BS>(A, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
+                         vblk, vslab, g, c, lane);
+    if (tg < tfull)
+      compute_group<T, D, false>(A, qop, o, m, l, 32, g, scale_log2);
+    else
+      compute_group<T, D, true>(A, qop, o, m, l, t1 - tg, g, scale_log2);
+  }
+#endif
 
   float lt = xor_sum(l, 16);
   lt = xor_sum(lt, 32);
@@ -276,7 +413,7 @@ __global__ __launch_bounds__(64) void decode_part_f32(
       float dot = 0.f;
 #pragma unroll 4
       for (int j = 0; j < D / X; ++j) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(kt + (j * BS + lane) * X);
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(kt + (j * BS + k_row<BS>(lane)) * X);
         dot = fmaf(qs[4 * j + 0], kv[0], dot);
         dot = fmaf(qs[4 * j + 1], kv[1], dot);
         dot = fmaf(qs[4 * j + 2], kv[2], dot);
@@ -325,33 +462,98 @@ __global__ __launch_bounds__(64) void decode_part_f32(
 }
 
 // Log-sum-exp merge of the partitions of one (sequence, query head):
-// M = max m_p, L = sum 2^(m_p - M) l_p, out = sum 2^(m_p - M) o_p / L, in
-// ascending p.  One thread per output dim.
+// M = max m_p, L = sum 2^(m_p - M) l_p, out = sum 2^(m_p - M) o_p / L.
+// One 256-thread work-group per (query head, sequence).  The weights go
+// through LDS in chunks of kReduceChunk partitions; thread (lane pl, dims
+// 4*d4 .. 4*d4+3) sums the partitions p = pl (mod PL) in ascending order with
+// 16-byte loads, and the PL partial sums are added in lane order, so the
+// result does not depend on timing.
+constexpr int kReduceThreads = 256;
+constexpr int kReduceChunk = 1024;
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  for (int mask = 32; mask >= 1; mask >>= 1) v = xor_max(v, mask);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < kReduceThreads / 64; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  for (int mask = 32; mask >= 1; mask >>= 1) v = xor_sum(v, mask);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < kReduceThreads / 64; ++i) r += red[i];
+  return r;
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_reduce(T* __restrict__ out,
-                                                   const float* __restrict__ ws_o,
-                                                   const float2* __restrict__ ws_ml,
-                                                   const int32_t* __restrict__ ctx_lens,
-                                                   int max_tokens, int H_q, int part, int maxP) {
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce(
+    T* __restrict__ out, const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
+    const int32_t* __restrict__ ctx_lens, int max_tokens, int H_q, int part, int maxP) {
+  constexpr int TPR = D / 4;                  // threads per partition row
+  constexpr int PL = kReduceThreads / TPR;    // partition lanes
+  __shared__ float sh_w[kReduceChunk];
+  __shared__ float sh_red[kReduceThreads / 64];
+  __shared__ f32x4 sh_acc[PL][TPR];
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
   const Span sp = partition_span(ctx_lens, s, max_tokens, part, 0);
   if (sp.nparts <= 1) return;
   const int np = sp.nparts < maxP ? sp.nparts : maxP;
   const int64_t row = static_cast<int64_t>(s) * H_q + h;
   const float2* ml = ws_ml + row * maxP;
-  const float* o = ws_o + row * maxP * D + d;
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[p].x);
-  float L = 0.f, acc = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float2 v = ml[p];
-    const float w = fast_exp2(v.x - M);
-    L = fmaf(w, v.y, L);
-    acc = fmaf(w, o[static_cast<int64_t>(p) * D], acc);
+  const f32x4* o4 = reinterpret_cast<const f32x4*>(ws_o + row * maxP * D);
+
+  float mx = -INFINITY;
+  for (int p = tid; p < np; p += kReduceThreads) mx = fmaxf(mx, ml[p].x);
+  const float M = block_max(mx, sh_red);
+
+  const int d4 = tid % TPR, pl = tid / TPR;
+  float lsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < np; base += kReduceChunk) {
+    const int n = np - base < kReduceChunk ? np - base : kReduceChunk;
+    __syncthreads();
+    for (int i = tid; i < n; i += kReduceThreads) {
+      const float2 v = ml[base + i];
+      const float w = fast_exp2(v.x - M);
+      sh_w[i] = w;
+      lsum = fmaf(w, v.y, lsum);
+    }
+    __syncthreads();
+    const f32x4* src = o4 + static_cast<int64_t>(base) * TPR + d4;
+    int i = pl;
+    for (; i + 3 * PL < n; i += 4 * PL) {
+      const f32x4 a0 = src[static_cast<int64_t>(i) * TPR];
+      const f32x4 a1 = src[static_cast<int64_t>(i + PL) * TPR];
+      const f32x4 a2 = src[static_cast<int64_t>(i + 2 * PL) * TPR];
+      const f32x4 a3 = src[static_cast<int64_t>(i + 3 * PL) * TPR];
+      acc += sh_w[i] * a0;
+      acc += sh_w[i + PL] * a1;
+      acc += sh_w[i + 2 * PL] * a2;
+      acc += sh_w[i + 3 * PL] * a3;
+    }
+    for (; i < n; i += PL) acc += sh_w[i] * src[static_cast<int64_t>(i) * TPR];
   }
-  out[row * D + d] = static_cast<T>(acc / L);
+  const float L = block_sum(lsum, sh_red);
+  sh_acc[pl][d4] = acc;
+  __syncthreads();
+  if (pl == 0) {
+    f32x4 t = sh_acc[0][d4];
+    for (int q = 1; q < PL; ++q) t += sh_acc[q][d4];
+    const float inv = 1.f / L;
+    T* dst = out + row * D + 4 * d4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[r] = static_cast<T>(t[r] * inv);
+  }
 }
 
 struct DecodeArgs {
@@ -379,7 +581,7 @@ void launch_mfma(const DecodeArgs& a) {
                      a.lens, a.max_tokens, a.H_q, a.H_kv, a.G, n_hg, a.num_blocks, a.scale_log2,
                      a.part, a.maxP);
   if (a.maxP > 1)
-    hipLaunchKernelGGL((decode_reduce<T, D>), dim3(a.H_q, a.B), dim3(D), 0, a.st,
+    hipLaunchKernelGGL((decode_reduce<T, D>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0, a.st,
                        static_cast<T*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens, a.H_q,
                        a.part, a.maxP);
 }
@@ -392,7 +594,7 @@ void launch_f32(const DecodeArgs& a) {
                      a.maxb, a.lens, a.max_tokens, a.H_q, a.H_kv, a.G, a.num_blocks,
                      a.scale_log2, a.part, a.maxP);
   if (a.maxP > 1)
-    hipLaunchKernelGGL((decode_reduce<float, D>), dim3(a.H_q, a.B), dim3(D), 0, a.st,
+    hipLaunchKernelGGL((decode_reduce<float, D>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0, a.st,
                        static_cast<float*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens, a.H_q,
                        a.part, a.maxP);
 }

@@ -32,8 +32,10 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const E* __restrict__ k_n
     const int tt = static_cast<int>(slot - b * BS);
     const int64_t src = (t * H + h) * D + jv * X;
     const int64_t tile = (b * H + h) * static_cast<int64_t>(BS) * D;
-    // K(b, h, tt, i) at tile + ((i / X) * BS + tt) * X + i % X
-    *reinterpret_cast<u32x4*>(kc + tile + (static_cast<int64_t>(jv) * BS + tt) * X) =
+    // K(b, h, tt, i) at tile + ((i / X) * BS + r(tt)) * X + i % X, where r puts
+    // the tokens with bit 2 clear first in each slab
+    const int kr = ((tt & 4) ? BS / 2 : 0) + 4 * (tt >> 3) + (tt & 3);
+    *reinterpret_cast<u32x4*>(kc + tile + (static_cast<int64_t>(jv) * BS + kr) * X) =
         *reinterpret_cast<const u32x4*>(k_new + src);
     // V(b, h, tt, i) at tile + ((tt / X) * D + i) * X + tt % X
     union {

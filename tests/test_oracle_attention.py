@@ -110,17 +110,30 @@ def test_bf16_rounding_of_inputs_is_rne():
 # layout
 # ----------------------------------------------------------------------------
 
+def test_k_row_order():
+    # tokens with bit 2 clear first, then with bit 2 set
+    assert [A.k_row(t, 16) for t in range(16)] == [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15]
+    order32 = sorted(range(32), key=lambda t: A.k_row(t, 32))
+    assert order32 == [0, 1, 2, 3, 8, 9, 10, 11, 16, 17, 18, 19, 24, 25, 26, 27,
+                       4, 5, 6, 7, 12, 13, 14, 15, 20, 21, 22, 23, 28, 29, 30, 31]
+
+
 def test_layout_hand_worked_offsets():
     # bf16 (x = 8), H = 2, bs = 16, d = 16.  Tile = 16 * 16 = 256 elements.
     # K(b=1, h=1, t=3, i=10): tile (1*2+1)=3 -> 768; slab i//8 = 1 -> +1*16*8 = 128;
-    #   token 3 -> +3*8 = 24; lane i%8 = 2 -> 768+128+24+2 = 922
+    #   token 3 sits in row 3 -> +3*8 = 24; lane i%8 = 2 -> 768+128+24+2 = 922
     assert A.k_offset(1, 1, 3, 10, H=2, bs=16, d=16, x=8) == 922
+    # K(b=0, h=0, t=5, i=0): token 5 has bit 2 set -> row 8 + 0 + 1 = 9 -> 9*8 = 72
+    assert A.k_offset(0, 0, 5, 0, H=2, bs=16, d=16, x=8) == 72
+    # K(b=0, h=1, t=9, i=17) with d = 32: tile 256*2 = 512; slab 2 -> +2*128 = 256;
+    #   token 9 (bit 2 clear) -> row 4 + 1 = 5 -> +40; lane 1 -> 809
+    assert A.k_offset(0, 1, 9, 17, H=2, bs=16, d=32, x=8) == 809
     # V(b=1, h=1, t=11, i=5): tile 768; slab t//8 = 1 -> +1*16*8 = 128; dim 5 -> +40;
     #   t%8 = 3 -> 768+128+40+3 = 939
     assert A.v_offset(1, 1, 11, 5, H=2, bs=16, d=16, x=8) == 939
     # fp32 (x = 4), H = 1, bs = 16, d = 8:
-    # K(0,0,t=5,i=6): slab 1 -> 64; token 5 -> 20; lane 2 -> 86
-    assert A.k_offset(0, 0, 5, 6, H=1, bs=16, d=8, x=4) == 86
+    # K(0,0,t=5,i=6): slab 1 -> 64; token 5 -> row 9 -> 36; lane 2 -> 102
+    assert A.k_offset(0, 0, 5, 6, H=1, bs=16, d=8, x=4) == 102
     # V(0,0,t=6,i=7): slab 1 -> 32; dim 7 -> 28; lane 2 -> 62
     assert A.v_offset(0, 0, 6, 7, H=1, bs=16, d=8, x=4) == 62
 
