@@ -42,7 +42,27 @@ def parse():
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="run only a 1 GiB device copy and fill of known size (for scaling "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def calibrate():
+    """Known-size traffic for counter calibration: 5 x (fill 1 GiB), then
+    5 x (copy 1 GiB -> 1 GiB)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate": True, "fill_bytes_written": n, "copy_bytes_read": n,
+                      "copy_bytes_written": n, "launches_each": 5}), flush=True)
 
 
 def source_hash() -> str:
@@ -137,6 +157,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU "
               "sharding of this path is design-only.", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate:
+        calibrate()
+        return
     import torch
     import paged_kv_cache_12_amd as pa
     from paged_kv_cache_12_amd.manager import PagedKVCache, storage_to_torch

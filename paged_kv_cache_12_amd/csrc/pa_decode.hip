@@ -26,14 +26,15 @@
 #ifndef PA_LAZY
 #define PA_LAZY 1
 #endif
-#ifndef PA_PIPE
-#define PA_PIPE 0
-#endif
 #ifndef PA_WAVES
-#define PA_WAVES 2
+#define PA_WAVES 3
 #endif
 
 namespace pa {
+
+// Tokens a work-group of the fp16/bf16 path aims to cover: NW partitions of
+// `part` tokens with NW = kChunkTokens / part (1..8), 8 waves when unsplit.
+constexpr int kChunkTokens = 2048;
 
 // Scores more than this many log2 units above the running reference trigger a
 // rescale; weights fed to the PV product are at most 2^kRescaleLog2.
@@ -84,6 +85,34 @@ __device__ __forceinline__ Span partition_span(const int32_t* ctx_lens, int s, i
   sp.nparts = part > 0 ? ((ctx + part - 1) / part > 1 ? (ctx + part - 1) / part : 1) : 1;
   sp.t0 = part > 0 ? p * part : 0;
   sp.t1 = part > 0 ? (ctx < sp.t0 + part ? ctx : sp.t0 + part) : ctx;
+  return sp;
+}
+
+struct ChunkSpan {
+  int nchunks, t0, t1;
+};
+
+// Token range of wave `wave` in chunk `ch` of sequence s: partition
+// ch * NW + wave of `part` tokens, or with part == 0 an even split of the whole
+// context into NW runs of whole 32-token groups.
+template <int NW>
+__device__ __forceinline__ ChunkSpan chunk_span(const int32_t* ctx_lens, int s, int max_tokens,
+                                                int part, int ch, int wave) {
+  ChunkSpan sp;
+  int ctx = ctx_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > max_tokens ? max_tokens : ctx);
+  int unit;
+  if (part > 0) {
+    const int nparts = (ctx + part - 1) / part;
+    sp.nchunks = nparts > NW ? (nparts + NW - 1) / NW : 1;
+    unit = part;
+  } else {
+    sp.nchunks = 1;
+    unit = (((ctx + NW - 1) / NW) + 31) & ~31;
+  }
+  const int64_t lo = (static_cast<int64_t>(ch) * NW + wave) * unit;
+  sp.t0 = lo < ctx ? static_cast<int>(lo) : ctx;
+  sp.t1 = lo + unit < ctx ? static_cast<int>(lo + unit) : ctx;
   return sp;
 }
 
@@ -242,30 +271,38 @@ __device__ __forceinline__ void compute_group(GroupTiles<T, D>& G,
   for (int j = 0; j < NJ; ++j) o[j] = M::mma(G.v[j], pop, o[j]);
 }
 
-template <typename T, int D, int BS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES)))
+// One work-group of NW wavefronts per (chunk, KV head [x head group],
+// sequence).  A chunk is NW consecutive partitions; wave w runs partition
+// chunk * NW + w with its own running state, and the NW states are merged
+// (log-sum-exp) in LDS, so one partial per chunk goes to memory.  Writes in
+// the middle of the KV read stream are expensive on this part (a few KiB per
+// work unit cost up to ~18 % of bandwidth), hence one write per NW partitions.
+// With part == 0 the context is one chunk split evenly across the waves.
+template <typename T, int D, int BS, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PA_WAVES)))
 void decode_part_mfma(
     T* __restrict__ out, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ block_tables, int maxb, const int32_t* __restrict__ ctx_lens,
     int max_tokens, int H_q, int H_kv, int G, int n_hg, int num_blocks, float scale_log2,
-    int part, int maxP) {
+    int part, int maxC) {
   typedef Mfma<T> M;
   typedef typename M::v8 v8;
   constexpr int NC = D / 32;    // QK k-chunks of 32 dims
   constexpr int NJ = D / 16;    // PV output chunks of 16 dims
   constexpr int TILE = BS * D;  // elements per (block, head) tile
 
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int c = lane & 15;  // MFMA row/column index within a lane group
   const int g = lane >> 4;  // lane group
-  const int p = blockIdx.x;
+  const int ch = blockIdx.x;
   const int kvh = blockIdx.y / n_hg;
   const int hg = blockIdx.y - kvh * n_hg;
   const int s = blockIdx.z;
 
-  const Span sp = partition_span(ctx_lens, s, max_tokens, part, p);
-  if (p >= sp.nparts) return;
+  const ChunkSpan sp = chunk_span<NW>(ctx_lens, s, max_tokens, part, ch, wave);
+  if (ch >= sp.nchunks) return;  // uniform over the work-group
   const int t0 = sp.t0, t1 = sp.t1;
 
   const int hin = hg * 16 + c;  // head within the GQA group
@@ -307,54 +344,71 @@ void decode_part_mfma(
   const int vblk = (8 * g) / BS;
   const int vslab = ((8 * g) % BS) / 8;
 
-  // Two register sets: group i+1 is loading while group i is computed.
   // Full 32-token groups, then at most one partial group at the end.
   const int tfull = t0 + ((t1 - t0) & ~31);
   const int nb_valid = (t1 + BS - 1) / BS;  // table entries inside the context
   TableWindow win;
   fill_window(win, bt, t0 / BS, nb_valid, num_blocks, lane);
-#if PA_PIPE
-  // Two register sets: group i+1 is loading while group i is computed.
-  GroupTiles<T, D> A, B;
-  if (t0 < t1)
-    load_group<T, D, BS>(A, win, bt, t0, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
-                         vblk, vslab, g, c, lane);
   int tg = t0;
-  while (tg < tfull) {
-    if (tg + 32 < t1)
-      load_group<T, D, BS>(B, win, bt, tg + 32, nb_valid, num_blocks, kh, vh, blk_stride, kblk,
-                           krow, vblk, vslab, g, c, lane);
-    compute_group<T, D, false>(A, qop, o, m, l, 32, g, scale_log2);
-    tg += 32;
-    if (tg >= tfull) {
-      if (tg < t1) compute_group<T, D, true>(B, qop, o, m, l, t1 - tg, g, scale_log2);
-      tg = t1;
-      break;
-    }
-    if (tg + 32 < t1)
-      load_group<T, D, BS>(A, win, bt, tg + 32, nb_valid, num_blocks, kh, vh, blk_stride, kblk,
-                           krow, vblk, vslab, g, c, lane);
-    compute_group<T, D, false>(B, qop, o, m, l, 32, g, scale_log2);
-    tg += 32;
-  }
-  if (tg < t1) compute_group<T, D, true>(A, qop, o, m, l, t1 - tg, g, scale_log2);
-#else
-  for (int tg = t0; tg < t1; tg += 32) {
+  for (; tg < tfull; tg += 32) {
     GroupTiles<T, D> A;
     load_group<T, D, BS>(A, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
                          vblk, vslab, g, c, lane);
-    if (tg < tfull)
-      compute_group<T, D, false>(A, qop, o, m, l, 32, g, scale_log2);
-    else
-      compute_group<T, D, true>(A, qop, o, m, l, t1 - tg, g, scale_log2);
+    compute_group<T, D, false>(A, qop, o, m, l, 32, g, scale_log2);
   }
-#endif
+  if (tg < t1) {
+    GroupTiles<T, D> A;
+    load_group<T, D, BS>(A, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
+                         vblk, vslab, g, c, lane);
+    compute_group<T, D, true>(A, qop, o, m, l, t1 - tg, g, scale_log2);
+  }
 
   float lt = xor_sum(l, 16);
   lt = xor_sum(lt, 32);
+
+  if constexpr (NW > 1) {
+    // Merge the waves' states: M = max m_w, weights 2^(m_w - M).
+    __shared__ float sh_m[NW][16];
+    __shared__ float sh_l[NW][16];
+    __shared__ f32x4 sh_o[NW - 1][NJ][64];
+    if (g == 0) {
+      sh_m[wave][c] = m;
+      sh_l[wave][c] = lt;
+    }
+    if (wave > 0) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) sh_o[wave - 1][j][lane] = o[j];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    float mw[NW];
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      mw[w] = sh_m[w][c];
+      mm = fmaxf(mm, mw[w]);
+    }
+    float f[NW];
+    float ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      f[w] = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - mm);
+      ls = fmaf(f[w], sh_l[w][c], ls);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      f32x4 acc = f[0] * o[j];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) acc += f[w] * sh_o[w - 1][j][lane];
+      o[j] = acc;
+    }
+    m = mm;
+    lt = ls;
+  }
+
   if (!hvalid) return;
   const int64_t row = static_cast<int64_t>(s) * H_q + qh;
-  if (sp.nparts == 1) {
+  if (sp.nchunks == 1) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     T* dst = out + row * D + 4 * g;
 #pragma unroll
@@ -362,10 +416,10 @@ void decode_part_mfma(
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[16 * j + r] = static_cast<T>(o[j][r] * inv);
   } else {
-    float* dst = ws_o + (row * maxP + p) * D + 4 * g;
+    float* dst = ws_o + (row * maxC + ch) * D + 4 * g;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = o[j];
-    if (g == 0) ws_ml[row * maxP + p] = make_float2(m, lt);
+    if (g == 0) ws_ml[row * maxC + ch] = make_float2(m, lt);
   }
 }
 
@@ -496,7 +550,8 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 template <typename T, int D>
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce(
     T* __restrict__ out, const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
-    const int32_t* __restrict__ ctx_lens, int max_tokens, int H_q, int part, int maxP) {
+    const int32_t* __restrict__ ctx_lens, int max_tokens, int H_q, int part, int maxP,
+    int per_chunk) {
   constexpr int TPR = D / 4;                  // threads per partition row
   constexpr int PL = kReduceThreads / TPR;    // partition lanes
   __shared__ float sh_w[kReduceChunk];
@@ -505,9 +560,11 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce(
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int tid = threadIdx.x;
+  // partials: one per chunk of per_chunk partitions of the sequence
   const Span sp = partition_span(ctx_lens, s, max_tokens, part, 0);
-  if (sp.nparts <= 1) return;
-  const int np = sp.nparts < maxP ? sp.nparts : maxP;
+  const int nchunks = (sp.nparts + per_chunk - 1) / per_chunk;
+  if (nchunks <= 1) return;
+  const int np = nchunks < maxP ? nchunks : maxP;
   const int64_t row = static_cast<int64_t>(s) * H_q + h;
   const float2* ml = ws_ml + row * maxP;
   const f32x4* o4 = reinterpret_cast<const f32x4*>(ws_o + row * maxP * D);
@@ -556,6 +613,15 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce(
   }
 }
 
+inline int num_partitions(int max_ctx, int part) {
+  if (part <= 0 || max_ctx <= part) return 1;
+  return (max_ctx + part - 1) / part;
+}
+
+inline int num_chunks(int nparts, int per_chunk) {
+  return nparts > per_chunk ? (nparts + per_chunk - 1) / per_chunk : 1;
+}
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -572,18 +638,36 @@ struct DecodeArgs {
   hipStream_t st;
 };
 
-template <typename T, int D, int BS>
-void launch_mfma(const DecodeArgs& a) {
+template <typename T, int D, int BS, int NW>
+void launch_mfma_nw(const DecodeArgs& a) {
   const int n_hg = (a.G + 15) / 16;
-  hipLaunchKernelGGL((decode_part_mfma<T, D, BS>), dim3(a.maxP, a.H_kv * n_hg, a.B), dim3(64), 0,
-                     a.st, static_cast<T*>(a.out), a.ws_o, a.ws_ml, static_cast<const T*>(a.q),
-                     static_cast<const T*>(a.kc), static_cast<const T*>(a.vc), a.bt, a.maxb,
-                     a.lens, a.max_tokens, a.H_q, a.H_kv, a.G, n_hg, a.num_blocks, a.scale_log2,
-                     a.part, a.maxP);
-  if (a.maxP > 1)
+  const int maxC = num_chunks(a.maxP, NW);
+  hipLaunchKernelGGL((decode_part_mfma<T, D, BS, NW>), dim3(maxC, a.H_kv * n_hg, a.B),
+                     dim3(64 * NW), 0, a.st, static_cast<T*>(a.out), a.ws_o, a.ws_ml,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.kc),
+                     static_cast<const T*>(a.vc), a.bt, a.maxb, a.lens, a.max_tokens, a.H_q,
+                     a.H_kv, a.G, n_hg, a.num_blocks, a.scale_log2, a.part, maxC);
+  if (maxC > 1)
     hipLaunchKernelGGL((decode_reduce<T, D>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0, a.st,
                        static_cast<T*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens, a.H_q,
-                       a.part, a.maxP);
+                       a.part, maxC, NW);
+}
+
+// Waves per work-group for a partition size (see kChunkTokens).
+inline int waves_per_group(int part) {
+  if (part <= 0) return 8;
+  const int want = kChunkTokens / part;
+  return want >= 8 ? 8 : want >= 4 ? 4 : want >= 2 ? 2 : 1;
+}
+
+template <typename T, int D, int BS>
+void launch_mfma(const DecodeArgs& a) {
+  switch (waves_per_group(a.part)) {
+    case 8: launch_mfma_nw<T, D, BS, 8>(a); break;
+    case 4: launch_mfma_nw<T, D, BS, 4>(a); break;
+    case 2: launch_mfma_nw<T, D, BS, 2>(a); break;
+    default: launch_mfma_nw<T, D, BS, 1>(a); break;
+  }
 }
 
 template <int D, int BS>
@@ -596,7 +680,7 @@ void launch_f32(const DecodeArgs& a) {
   if (a.maxP > 1)
     hipLaunchKernelGGL((decode_reduce<float, D>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0, a.st,
                        static_cast<float*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens, a.H_q,
-                       a.part, a.maxP);
+                       a.part, a.maxP, 1);
 }
 
 template <typename T>
@@ -607,10 +691,6 @@ void dispatch_mfma(const DecodeArgs& a, int D, int BS) {
   else launch_mfma<T, 128, 32>(a);
 }
 
-inline int num_partitions(int max_ctx, int part) {
-  if (part <= 0 || max_ctx <= part) return 1;
-  return (max_ctx + part - 1) / part;
-}
 
 }  // namespace pa
 

@@ -130,7 +130,7 @@ WORKLOADS = {
         description="1 layer, batch 4, 4 heads (MHA), d 64, bs 16, ctx U[1,200], pool 64"),
     "llama3_8b_gqa_bf16": Workload(
         name="llama3_8b_gqa_bf16", dtype="bf16", batch=64, h_q=32, h_kv=8, head_dim=128,
-        block_size=16, seed=102, ctx_lo=512, ctx_hi=4096, step_append=True, partition=256,
+        block_size=16, seed=102, ctx_lo=512, ctx_hi=4096, step_append=True, partition=0,
         description="Llama-3-8B-class layer: 32 q / 8 kv heads, d 128, bs 16, batch 64, "
                     "ctx U[512,4096] + one appended token per step"),
     "opt13b_sampling_fp16": Workload(

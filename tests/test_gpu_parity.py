@@ -187,6 +187,7 @@ def run_both(sc, partition, rows=None, guard=1):
     ("f16", 40, 40, 128, 16, 512), ("f16", 8, 8, 64, 32, 64),
     ("bf16", 16, 1, 64, 16, 128), ("bf16", 64, 2, 128, 16, 256),   # G = 16, G = 32 (two head groups)
     ("f16", 12, 4, 128, 32, 0),
+    ("bf16", 32, 8, 128, 16, 1024), ("f16", 16, 4, 64, 32, 2048),   # 2 and 1 waves per group
 ])
 @pytest.mark.parametrize("peaked", [False, True])
 def test_decode_small(dtype, h_q, h_kv, d, bs, part, peaked):
