@@ -104,6 +104,20 @@ def fill_cache(sc, cache, dev):
     torch.cuda.synchronize()
 
 
+def unique_kv_bytes(tables, lens, wl):
+    """KV bytes of the distinct physical blocks the batch reads (a block
+    aliased by several sequences counts once, with its filled positions)."""
+    seen = {}
+    bs = wl.block_size
+    for row, n in zip(tables, lens):
+        nb = -(-int(n) // bs)
+        for j in range(nb):
+            b = int(row[j])
+            fill = min(bs, int(n) - j * bs)
+            seen[b] = max(seen.get(b, 0), fill)
+    return float(sum(seen.values())) * 2 * wl.h_kv * wl.head_dim * synth.ELEM_BYTES[wl.dtype]
+
+
 def cpu_baseline(sc, budget_s: float):
     """Time the oracle (as it stands) on a bounded sample of the same workload:
     its pool model and cache writes set up the sample, then paged_decode over
@@ -184,54 +198,42 @@ def main():
     q = storage_to_torch(sc.q, wl.dtype).to(dev)
     out = torch.empty_like(q)
     ws_bytes = pa.pa_decode_workspace_size(B, wl.h_q, wl.head_dim, max_ctx_end, part)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    step_bytes = []
+
     if appends:
+        # one native call per step: pool append, one metadata copy, COW copies,
+        # block write, decode (pa_decode_step); pinned staging alternates
         step_k = storage_to_torch(sc.step_k, wl.dtype).to(dev)
         step_v = storage_to_torch(sc.step_v, wl.dtype).to(dev)
+        sbytes = pa.pa_decode_step_staging_size(B, maxb)
+        h_stage = [torch.empty(sbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        d_stage = torch.empty(sbytes, dtype=torch.uint8, device=dev)
+        done = [None, None]
+        fill = int(lens0.sum())
 
-    # pinned host staging, double buffered
-    nbuf = 2
-    h_tab = [torch.empty((B, maxb), dtype=torch.int32, pin_memory=True) for _ in range(nbuf)]
-    h_len = [torch.empty(B, dtype=torch.int32, pin_memory=True) for _ in range(nbuf)]
-    h_slot = [torch.empty(B, dtype=torch.int64, pin_memory=True) for _ in range(nbuf)]
-    d_tab = [torch.empty((B, maxb), dtype=torch.int32, device=dev) for _ in range(nbuf)]
-    d_len = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(nbuf)]
-    d_slot = [torch.empty(B, dtype=torch.int64, device=dev) for _ in range(nbuf)]
-    copied = [None] * nbuf
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(total_steps)]
-    ctx_bytes = []
+        def step(i):
+            j = i & 1
+            if done[j] is not None:
+                done[j].synchronize()      # staging buffer j is free again
+            pa.pa_decode_step(cache.pool, seqs, step_k, step_v, cache.k_cache, cache.v_cache,
+                              q, out, wl.scale, part, maxb, h_stage[j], d_stage, ws)
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            done[j] = ev
+            step_bytes.append(float(fill + B * (i + 1)) * 2 * wl.h_kv * wl.head_dim * e)
+    else:
+        tab_h, len_h = cache.tables(seqs, maxb)
+        d_tab = torch.from_numpy(tab_h).to(dev)
+        d_len = torch.from_numpy(len_h).to(dev)
+        max_ctx0 = int(len_h.max())
+        kv0 = float(len_h.sum()) * 2 * wl.h_kv * wl.head_dim * e
 
-    def step(i):
-        j = i % nbuf
-        if copied[j] is not None:
-            copied[j].synchronize()        # host buffer j is free again
-        if appends:
-            st, slots, pairs = cache.pool.append_batch(seqs, 1, slots_out=h_slot[j].numpy())
-            if st != pa.PA_OK:
-                raise pa.PAError(st, "append_batch")
-        else:
-            pairs = ()
-        cache.pool.block_tables(seqs, maxb, out=h_tab[j].numpy(), lens_out=h_len[j].numpy())
-        ctx_bytes.append(float(h_len[j].numpy().sum()) * 2 * wl.h_kv * wl.head_dim * e)
-        max_ctx = int(h_len[j].numpy().max())
-        d_tab[j].copy_(h_tab[j], non_blocking=True)
-        d_len[j].copy_(h_len[j], non_blocking=True)
-        if appends:
-            d_slot[j].copy_(h_slot[j], non_blocking=True)
-        ce = torch.cuda.Event()
-        ce.record(stream)
-        copied[j] = ce
-        if len(pairs):
-            dp = torch.from_numpy(np.ascontiguousarray(pairs)).to(dev, non_blocking=False)
-            pa.pa_copy_blocks(cache.k_cache, cache.v_cache, dp)
-        if appends:
-            pa.pa_write_kv(step_k, step_v, cache.k_cache, cache.v_cache, d_slot[j])
-        ev[i][0].record(stream)
-        pa.pa_decode(out, q, cache.k_cache, cache.v_cache, d_tab[j], d_len[j], max_ctx, wl.scale,
-                     part, workspace=ws)
-        ev[i][1].record(stream)
+        def step(i):
+            pa.pa_decode(out, q, cache.k_cache, cache.v_cache, d_tab, d_len, max_ctx0,
+                         wl.scale, part, workspace=ws)
+            step_bytes.append(kv0)
 
     for i in range(args.warmup):
         step(i)
@@ -242,11 +244,30 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, total_steps)]
-    dec_ms_mean = float(np.mean(dec_ms))
-    kv_step = float(np.mean(ctx_bytes[args.warmup:]))
+    kv_step = float(np.mean(step_bytes[args.warmup:]))
     value = kv_step / (ms_step * 1e-3) / 1e9
-    achieved = kv_step / (dec_ms_mean * 1e-3) / 1e9
+
+    # the dominant kernel: pa_decode alone on the final tables, HIP events on
+    # its stream
+    tab_h, len_h = cache.tables(seqs, maxb)
+    d_tab = torch.from_numpy(tab_h).to(dev)
+    d_len = torch.from_numpy(len_h).to(dev)
+    max_ctx = int(len_h.max())
+    kv_dec = float(len_h.sum()) * 2 * wl.h_kv * wl.head_dim * e
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for _ in range(3):
+        pa.pa_decode(out, q, cache.k_cache, cache.v_cache, d_tab, d_len, max_ctx, wl.scale, part,
+                     workspace=ws)
+    for a0, a1 in evs:
+        a0.record(stream)
+        pa.pa_decode(out, q, cache.k_cache, cache.v_cache, d_tab, d_len, max_ctx, wl.scale, part,
+                     workspace=ws)
+        a1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms_mean = float(np.mean([a0.elapsed_time(a1) for a0, a1 in evs]))
+    achieved = kv_dec / (dec_ms_mean * 1e-3) / 1e9
+    unique = unique_kv_bytes(tab_h, len_h, wl)
 
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
@@ -270,7 +291,7 @@ def main():
         "data": "synthetic (seeded N(0,1) K/V/q, no weights)",
         "config": {"workload": wl.name, "batch": B, "q_heads": wl.h_q, "kv_heads": wl.h_kv,
                    "head_dim": wl.head_dim, "block_size": wl.block_size, "partition": part,
-                   "mean_context": round(kv_step / (2 * wl.h_kv * wl.head_dim * e) / B, 1),
+                   "mean_context": round(kv_dec / (2 * wl.h_kv * wl.head_dim * e) / B, 1),
                    "step": ("append 1 token/seq + " if appends else "") + "decode",
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -278,8 +299,12 @@ def main():
         "decode_ms_mean": round(dec_ms_mean, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "pa_decode (partition + reduce)",
-                     "bytes_per_launch": round(kv_step)},
+                     "traffic": traffic,
+                     "kernel": "pa_decode" + (" (partition kernel + reduce)"
+                                              if ws_bytes else " (one kernel)"),
+                     "bytes_per_launch": round(kv_dec),
+                     "unique_bytes_per_launch": round(unique),
+                     "unique_achieved": round(unique / (dec_ms_mean * 1e-3) / 1e9, 1)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(sc, args.cpu_seconds)

@@ -59,6 +59,8 @@
 extern "C" {
 #endif
 
+typedef struct pa_pool pa_pool; /* host block pool, below */
+
 typedef enum {
   PA_OK = 0,
   PA_ERR_INVALID = 1,
@@ -156,6 +158,39 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int num_blocks, float scale, int partition_size, void* workspace,
                     size_t workspace_bytes, int dtype, void* stream);
 
+/*
+ * pa_decode_step — one decode iteration of a batch as the central manager
+ * hands it to the GPU (encyclopedia entry, "como funciona": the manager ships
+ * the block tables with each iteration's input): append one position to each
+ * of seqs[0..num_seqs) in the pool, build slots, copy-on-write pairs, lengths
+ * and block tables in `host_staging`, copy them to `dev_staging` with one
+ * asynchronous host-to-device copy, then run pa_copy_blocks (if any pair),
+ * pa_write_kv of k_new / v_new (device [num_seqs][H_kv][d]) into the new
+ * positions, and pa_decode of q into out (device [num_seqs][H_q][d]).
+ *
+ *   host_staging  pinned host memory, >= pa_decode_step_staging_size() bytes,
+ *                 16-byte aligned; read by the asynchronous copy, so it must
+ *                 not be rewritten until the stream has passed this call
+ *                 (alternate two buffers and wait on an event)
+ *   dev_staging   device memory of the same size; holds the step's metadata
+ *                 until the step's kernels have run
+ *   workspace     as for pa_decode, sized for the longest context after the
+ *                 append
+ * Every argument is checked before the pool changes: on any error status the
+ * pool and the device are untouched (PA_ERR_NO_BLOCKS when the pool cannot
+ * cover the batch, PA_ERR_INVALID when a table would exceed
+ * max_blocks_per_seq or the workspace is too small).  The caller owns all
+ * memory; nothing is allocated.
+ */
+size_t pa_decode_step_staging_size(int num_seqs, int max_blocks_per_seq);
+pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_seqs, const void* k_new,
+                         const void* v_new, void* k_cache, void* v_cache, int num_blocks,
+                         int num_kv_heads, int head_dim, int block_size, const void* q,
+                         void* out, int num_q_heads, float scale, int partition_size,
+                         int max_blocks_per_seq, void* host_staging, void* dev_staging,
+                         size_t staging_bytes, void* workspace, size_t workspace_bytes,
+                         int dtype, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host block pool (host memory only; no HIP calls)                          */
 /* ------------------------------------------------------------------------ */
@@ -169,8 +204,6 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * partly filled and held by another sequence (the appending sequence copies;
  * the last holder writes in place).  Appends are all-or-nothing.
  */
-typedef struct pa_pool pa_pool;
-
 pa_status pa_pool_create(int num_blocks, int block_size, const int32_t* free_order,
                          pa_pool** out);
 void pa_pool_destroy(pa_pool* pool);

@@ -36,6 +36,9 @@ SIGNATURES = {
     "pa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "pa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i,
                        _vp, _sz, _i, _vp]),
+    "pa_decode_step_staging_size": (_sz, [_i, _i]),
+    "pa_decode_step": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _f,
+                            _i, _i, _vp, _vp, _sz, _vp, _sz, _i, _vp]),
     "pa_pool_create": (_i, [_i, _i, _vp, _c.POINTER(_vp)]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_seq_create": (_i, [_vp, _i64]),
@@ -202,6 +205,31 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
                          ws_ptr, ws_bytes, torch_dtype_code(q), _stream_ptr(stream))
     _check(st, "pa_decode")
     return workspace
+
+
+def pa_decode_step_staging_size(num_seqs: int, max_blocks_per_seq: int) -> int:
+    return int(lib().pa_decode_step_staging_size(num_seqs, max_blocks_per_seq))
+
+
+def pa_decode_step(pool: "Pool", seqs: np.ndarray, k_new, v_new, k_cache, v_cache, q, out,
+                   scale: float, partition_size: int, max_blocks_per_seq: int, host_staging,
+                   dev_staging, workspace, stream=None):
+    """seqs: int64 numpy array; host_staging: pinned uint8 CPU tensor; dev_staging,
+    workspace: uint8 GPU tensors; the rest GPU tensors as for pa_write_kv / pa_decode."""
+    nb, H_kv, bs, d = cache_geometry(k_cache, v_cache)
+    B, H_q, _ = q.shape
+    if not host_staging.is_pinned():
+        raise ValueError("host_staging must be pinned host memory")
+    sbytes = min(host_staging.numel(), dev_staging.numel())
+    st = lib().pa_decode_step(pool._h, _np_ptr(seqs), B, _dev_ptr(k_new, "k_new"),
+                              _dev_ptr(v_new, "v_new"), _dev_ptr(k_cache, "k_cache"),
+                              _dev_ptr(v_cache, "v_cache"), nb, H_kv, d, bs, _dev_ptr(q, "q"),
+                              _dev_ptr(out, "out"), H_q, float(scale), partition_size,
+                              max_blocks_per_seq, host_staging.data_ptr(),
+                              _dev_ptr(dev_staging, "dev_staging"), sbytes,
+                              _dev_ptr(workspace, "workspace"), workspace.numel(),
+                              torch_dtype_code(q), _stream_ptr(stream))
+    _check(st, "pa_decode_step")
 
 
 def pa_kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, dtype: int) -> int:

@@ -33,7 +33,7 @@ def L():
 
 def test_library_exports_exactly_the_header_functions(L):
     declared = header_functions()
-    assert len(declared) == 19
+    assert len(declared) == 21
     for name in declared:
         assert hasattr(L, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
@@ -228,3 +228,43 @@ def test_block_tables_capacity_errors(L):
         pool.block_tables([0], 2)          # needs 3 entries
     with pytest.raises(pa.PAError):
         pool.block_tables([5], 4)          # unknown id
+
+
+# ----------------------------------------------------------------------------
+# pa_decode_step: every rejection happens before the pool changes
+# ----------------------------------------------------------------------------
+
+def _step(L, pool, seqs, **kw):
+    a = dict(k_new=16, v_new=16, kc=16, vc=16, nb=64, H_kv=2, d=128, bs=16, q=16, out=16,
+             H_q=8, scale=0.1, part=0, maxb=8, hs=16, ds=16, sbytes=1 << 20, ws=None,
+             ws_bytes=0, dt=2)
+    a.update(kw)
+    s = np.ascontiguousarray(seqs, dtype=np.int64)
+    return L.pa_decode_step(pool._h, s.ctypes.data_as(ctypes.c_void_p), s.size, a["k_new"],
+                            a["v_new"], a["kc"], a["vc"], a["nb"], a["H_kv"], a["d"], a["bs"],
+                            a["q"], a["out"], a["H_q"], a["scale"], a["part"], a["maxb"],
+                            a["hs"], a["ds"], a["sbytes"], a["ws"], a["ws_bytes"], a["dt"], None)
+
+
+def test_decode_step_rejects_before_touching_the_pool(L):
+    pool = pa.Pool(64, 16, list(range(64)))
+    pool.create(0)
+    pool.append(0, 32)            # full last block: the next append takes a new block
+    pool.create(1)
+    pool.append(1, 5)
+    before = (pool.free_list().tolist(), pool.stats())
+    INV, UNS = pa.PA_ERR_INVALID, pa.PA_ERR_UNSUPPORTED
+    assert _step(L, pool, [0, 1], maxb=2) == INV          # seq 0 would need 3 blocks
+    assert _step(L, pool, [0, 1], d=96) == UNS
+    assert _step(L, pool, [0, 1], H_q=6, H_kv=4) == INV
+    assert _step(L, pool, [0, 1], sbytes=64) == INV       # staging too small
+    assert _step(L, pool, [0, 1], q=24) == INV            # misaligned
+    assert _step(L, pool, [0, 1], part=32) == INV         # needs a workspace, none given
+    assert _step(L, pool, [0, 7]) == pa.PA_ERR_UNKNOWN_SEQ
+    assert _step(L, pool, [0, 0]) == INV                  # duplicate ids (append rejects)
+    full = pa.Pool(2, 16, [0, 1])
+    full.create(0)
+    full.append(0, 32)
+    assert _step(L, full, [0]) == pa.PA_ERR_NO_BLOCKS
+    assert (pool.free_list().tolist(), pool.stats()) == before
+    assert pa.pa_decode_step_staging_size(64, 257) == 512 + 512 + 256 + (64 * 257 * 4 + 255) // 256 * 256
