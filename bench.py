@@ -201,6 +201,8 @@ def main():
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     step_bytes = []
+    # aliased blocks (forks, shared prefixes): cached loads
+    flags = pa.PA_DECODE_SHARED_KV if cache.pool.stats()["shared"] > 0 else 0
 
     if appends:
         # one native call per step: pool append, one metadata copy, COW copies,
@@ -232,7 +234,7 @@ def main():
 
         def step(i):
             pa.pa_decode(out, q, cache.k_cache, cache.v_cache, d_tab, d_len, max_ctx0,
-                         wl.scale, part, workspace=ws)
+                         wl.scale, part, workspace=ws, flags=flags)
             step_bytes.append(kv0)
 
     for i in range(args.warmup):
@@ -258,11 +260,11 @@ def main():
            for _ in range(args.steps)]
     for _ in range(3):
         pa.pa_decode(out, q, cache.k_cache, cache.v_cache, d_tab, d_len, max_ctx, wl.scale, part,
-                     workspace=ws)
+                     workspace=ws, flags=flags)
     for a0, a1 in evs:
         a0.record(stream)
         pa.pa_decode(out, q, cache.k_cache, cache.v_cache, d_tab, d_len, max_ctx, wl.scale, part,
-                     workspace=ws)
+                     workspace=ws, flags=flags)
         a1.record(stream)
     torch.cuda.synchronize()
     dec_ms_mean = float(np.mean([a0.elapsed_time(a1) for a0, a1 in evs]))

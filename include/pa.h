@@ -72,6 +72,15 @@ typedef enum {
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
 
+/* pa_decode flags */
+enum {
+  /* Blocks of the batch may be aliased by several sequences (forks, shared
+   * prefixes): K/V are read with ordinary cached loads so aliased blocks are
+   * served from L2 / Infinity Cache.  Without it K/V are read with
+   * non-temporal loads (each block read once per step). */
+  PA_DECODE_SHARED_KV = 1
+};
+
 /* Static text for a status code; "unknown status" for other values. */
 const char* pa_status_str(int status);
 
@@ -144,6 +153,7 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  *        are merged by a log-sum-exp reduce in a fixed order
  *   workspace  device, >= pa_decode_workspace_size(...) bytes (may be NULL
  *        when that is 0); contents on entry are ignored
+ *   flags  0 or PA_DECODE_SHARED_KV (a cache policy; results are identical)
  *
  * out[s][h] = softmax(scale * q[s][h] . K_s[:, h/G]) V_s[:, h/G], G = H_q/H_kv,
  * where K_s, V_s are the sequence's tokens in logical order.  A sequence with
@@ -156,7 +166,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     const int32_t* context_lens, int num_seqs, int max_context_len,
                     int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                     int num_blocks, float scale, int partition_size, void* workspace,
-                    size_t workspace_bytes, int dtype, void* stream);
+                    size_t workspace_bytes, int dtype, int flags, void* stream);
 
 /*
  * pa_decode_step — one decode iteration of a batch as the central manager
@@ -166,7 +176,9 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * and block tables in `host_staging`, copy them to `dev_staging` with one
  * asynchronous host-to-device copy, then run pa_copy_blocks (if any pair),
  * pa_write_kv of k_new / v_new (device [num_seqs][H_kv][d]) into the new
- * positions, and pa_decode of q into out (device [num_seqs][H_q][d]).
+ * positions, and pa_decode of q into out (device [num_seqs][H_q][d]).  The
+ * decode issues the longest contexts first and sets PA_DECODE_SHARED_KV
+ * itself whenever the pool holds a block with refcount > 1.
  *
  *   host_staging  pinned host memory, >= pa_decode_step_staging_size() bytes,
  *                 16-byte aligned; read by the asynchronous copy, so it must

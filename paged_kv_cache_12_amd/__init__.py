@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libpa.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_UNKNOWN_SEQ, PA_ERR_HIP = range(6)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_DECODE_SHARED_KV = 1
 DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
 
 # name -> (restype, argtypes), mirroring include/pa.h
@@ -35,7 +36,7 @@ SIGNATURES = {
     "pa_copy_blocks": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "pa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "pa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i,
-                       _vp, _sz, _i, _vp]),
+                       _vp, _sz, _i, _i, _vp]),
     "pa_decode_step_staging_size": (_sz, [_i, _i]),
     "pa_decode_step": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _f,
                             _i, _i, _vp, _vp, _sz, _vp, _sz, _i, _vp]),
@@ -179,7 +180,8 @@ def pa_decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int,
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
-              scale: float, partition_size: int = 512, workspace=None, stream=None):
+              scale: float, partition_size: int = 512, workspace=None, stream=None,
+              flags: int = 0):
     """out, q [B][H_q][d]; block_tables int32 [B][maxb]; context_lens int32 [B]."""
     torch = _torch()
     nb, H_kv, bs, d = cache_geometry(k_cache, v_cache)
@@ -202,7 +204,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
                          _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables"),
                          block_tables.shape[1], _dev_ptr(context_lens, "context_lens"), B,
                          max_context_len, H_q, H_kv, d, bs, nb, float(scale), partition_size,
-                         ws_ptr, ws_bytes, torch_dtype_code(q), _stream_ptr(stream))
+                         ws_ptr, ws_bytes, torch_dtype_code(q), flags, _stream_ptr(stream))
     _check(st, "pa_decode")
     return workspace
 

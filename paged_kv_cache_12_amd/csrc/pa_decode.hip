@@ -116,6 +116,35 @@ __device__ __forceinline__ ChunkSpan chunk_span(const int32_t* ctx_lens, int s, 
   return sp;
 }
 
+// Grid linearisation.  Streaming (no aliased blocks): chunk fastest, then
+// head, then sequence.  Aliased blocks: work-groups are dealt to the 8 XCDs
+// round-robin by linear id, so with (KV head x head group) count HG a multiple
+// of 8 the id is split as id = 8 j + x: XCD x serves heads x, x+8, ...; along
+// j the head varies fastest, then the sequence, then the chunk, and sequences
+// that alias the same blocks (shared prefixes, parallel samples) read them one
+// after the other from the same XCD's L2.
+struct WorkItem {
+  int chunk, hgl, seq;
+};
+
+template <bool ALIASED>
+__device__ __forceinline__ WorkItem work_item(int id, int HG, int B, int maxC) {
+  WorkItem w;
+  if (!ALIASED || (HG & 7) != 0) {
+    w.chunk = id % maxC;
+    const int rest = id / maxC;
+    w.hgl = rest % HG;
+    w.seq = rest / HG;
+    return w;
+  }
+  const int x = id & 7, j = id >> 3, sub = HG >> 3;
+  w.hgl = x + 8 * (j % sub);
+  const int rest = j / sub;
+  w.seq = rest % B;
+  w.chunk = rest / B;
+  return w;
+}
+
 // Registers holding one 32-token group's operands.
 template <typename T, int D>
 struct GroupTiles {
@@ -124,10 +153,12 @@ struct GroupTiles {
   v8 v[D / 16];
 };
 
-// K/V tiles are read once per step: non-temporal loads.
-template <typename V>
+// K/V tile loads: non-temporal when every block is read once per step (NT),
+// ordinary cached loads when blocks are aliased by several sequences.
+template <typename V, bool NT>
 __device__ __forceinline__ V load16(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  return *reinterpret_cast<const V*>(p);
 }
 
 // Row of token t inside a K slab (tokens with bit 2 clear first).
@@ -155,7 +186,7 @@ __device__ __forceinline__ void fill_window(TableWindow& w, const int32_t* __res
   w.ids = b;
 }
 
-template <typename T, int D, int BS>
+template <typename T, int D, int BS, bool NT>
 __device__ __forceinline__ void load_group(GroupTiles<T, D>& G, TableWindow& w,
                                            const int32_t* __restrict__ bt, int tg, int nb_valid,
                                            int num_blocks, const T* kh, const T* vh,
@@ -173,11 +204,11 @@ __device__ __forceinline__ void load_group(GroupTiles<T, D>& G, TableWindow& w,
     const T* base = kh + pb[kblk[h]] * blk_stride + krow[h] * 8;
 #pragma unroll
     for (int k = 0; k < NC; ++k)
-      G.k[h][k] = load16<v8>(base + (4 * k + g) * (BS * 8));
+      G.k[h][k] = load16<v8, NT>(base + (4 * k + g) * (BS * 8));
   }
   const T* base = vh + pb[vblk] * blk_stride + vslab * (D * 8) + c * 8;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) G.v[j] = load16<v8>(base + 16 * j * 8);
+  for (int j = 0; j < NJ; ++j) G.v[j] = load16<v8, NT>(base + 16 * j * 8);
 }
 
 // QK, online-softmax update and PV for one 32-token group.  TAIL: only the
@@ -278,14 +309,14 @@ __device__ __forceinline__ void compute_group(GroupTiles<T, D>& G,
 // the middle of the KV read stream are expensive on this part (a few KiB per
 // work unit cost up to ~18 % of bandwidth), hence one write per NW partitions.
 // With part == 0 the context is one chunk split evenly across the waves.
-template <typename T, int D, int BS, int NW>
+template <typename T, int D, int BS, int NW, bool NT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PA_WAVES)))
 void decode_part_mfma(
     T* __restrict__ out, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ block_tables, int maxb, const int32_t* __restrict__ ctx_lens,
-    int max_tokens, int H_q, int H_kv, int G, int n_hg, int num_blocks, float scale_log2,
-    int part, int maxC) {
+    const int32_t* __restrict__ order, int B, int max_tokens, int H_q, int H_kv, int G,
+    int n_hg, int num_blocks, float scale_log2, int part, int maxC) {
   typedef Mfma<T> M;
   typedef typename M::v8 v8;
   constexpr int NC = D / 32;    // QK k-chunks of 32 dims
@@ -296,10 +327,12 @@ void decode_part_mfma(
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;  // MFMA row/column index within a lane group
   const int g = lane >> 4;  // lane group
-  const int ch = blockIdx.x;
-  const int kvh = blockIdx.y / n_hg;
-  const int hg = blockIdx.y - kvh * n_hg;
-  const int s = blockIdx.z;
+  const WorkItem wi = work_item<!NT>(blockIdx.x, H_kv * n_hg, B, maxC);
+  const int ch = wi.chunk;
+  const int kvh = wi.hgl / n_hg;
+  const int hg = wi.hgl - kvh * n_hg;
+  const int s = order ? order[wi.seq] : wi.seq;
+  if (s < 0 || s >= B) return;
 
   const ChunkSpan sp = chunk_span<NW>(ctx_lens, s, max_tokens, part, ch, wave);
   if (ch >= sp.nchunks) return;  // uniform over the work-group
@@ -352,13 +385,13 @@ void decode_part_mfma(
   int tg = t0;
   for (; tg < tfull; tg += 32) {
     GroupTiles<T, D> A;
-    load_group<T, D, BS>(A, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
+    load_group<T, D, BS, NT>(A, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
                          vblk, vslab, g, c, lane);
     compute_group<T, D, false>(A, qop, o, m, l, 32, g, scale_log2);
   }
   if (tg < t1) {
     GroupTiles<T, D> A;
-    load_group<T, D, BS>(A, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
+    load_group<T, D, BS, NT>(A, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
                          vblk, vslab, g, c, lane);
     compute_group<T, D, true>(A, qop, o, m, l, t1 - tg, g, scale_log2);
   }
@@ -623,6 +656,8 @@ inline int num_chunks(int nparts, int per_chunk) {
 }
 
 struct DecodeArgs {
+  const int32_t* order;  // optional sequence order (a permutation of 0..B-1)
+  bool shared_kv;        // blocks may be aliased: cached loads
   void* out;
   const void* q;
   const void* kc;
@@ -638,15 +673,25 @@ struct DecodeArgs {
   hipStream_t st;
 };
 
-template <typename T, int D, int BS, int NW>
-void launch_mfma_nw(const DecodeArgs& a) {
+template <typename T, int D, int BS, int NW, bool NT>
+void launch_part(const DecodeArgs& a, int maxC) {
   const int n_hg = (a.G + 15) / 16;
-  const int maxC = num_chunks(a.maxP, NW);
-  hipLaunchKernelGGL((decode_part_mfma<T, D, BS, NW>), dim3(maxC, a.H_kv * n_hg, a.B),
+  const int64_t grid = static_cast<int64_t>(maxC) * a.H_kv * n_hg * a.B;
+  hipLaunchKernelGGL((decode_part_mfma<T, D, BS, NW, NT>), dim3(static_cast<unsigned>(grid)),
                      dim3(64 * NW), 0, a.st, static_cast<T*>(a.out), a.ws_o, a.ws_ml,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.kc),
-                     static_cast<const T*>(a.vc), a.bt, a.maxb, a.lens, a.max_tokens, a.H_q,
-                     a.H_kv, a.G, n_hg, a.num_blocks, a.scale_log2, a.part, maxC);
+                     static_cast<const T*>(a.vc), a.bt, a.maxb, a.lens, a.order, a.B,
+                     a.max_tokens, a.H_q, a.H_kv, a.G, n_hg, a.num_blocks, a.scale_log2, a.part,
+                     maxC);
+}
+
+template <typename T, int D, int BS, int NW>
+void launch_mfma_nw(const DecodeArgs& a) {
+  const int maxC = num_chunks(a.maxP, NW);
+  if (a.shared_kv)
+    launch_part<T, D, BS, NW, false>(a, maxC);
+  else
+    launch_part<T, D, BS, NW, true>(a, maxC);
   if (maxC > 1)
     hipLaunchKernelGGL((decode_reduce<T, D>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0, a.st,
                        static_cast<T*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens, a.H_q,
@@ -708,13 +753,17 @@ PA_EXPORT size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int hea
   return o_bytes + rows * sizeof(float2);
 }
 
-PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* block_tables, int max_blocks_per_seq,
-                              const int32_t* context_lens, int num_seqs, int max_context_len,
-                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                              int num_blocks, float scale, int partition_size, void* workspace,
-                              size_t workspace_bytes, int dtype, void* stream) {
+namespace pa {
+
+pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int num_seqs, int max_context_len,
+                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, float scale, int partition_size, void* workspace,
+                      size_t workspace_bytes, int dtype, int flags, const int32_t* order,
+                      void* stream) {
   if (elem_bytes(dtype) == 0) return PA_ERR_UNSUPPORTED;
+  if (flags & ~PA_DECODE_SHARED_KV) return PA_ERR_INVALID;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_context_len < 0 || max_blocks_per_seq < 0 || partition_size < 0)
     return PA_ERR_INVALID;
@@ -731,13 +780,15 @@ PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* k_cache, con
     return PA_ERR_INVALID;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_ERR_INVALID;
-  if (num_seqs > 65535 || static_cast<int64_t>(num_kv_heads) * 16 > 65535) return PA_ERR_INVALID;
+  if (num_seqs > 65535 || num_q_heads > 65535) return PA_ERR_INVALID;
   const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
                                                partition_size);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PA_ERR_INVALID;
 
   DecodeArgs a;
+  a.order = order;
+  a.shared_kv = (flags & PA_DECODE_SHARED_KV) != 0;
   a.out = out;
   a.q = q;
   a.kc = k_cache;
@@ -776,4 +827,18 @@ PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* k_cache, con
       break;
   }
   return launch_status();
+}
+
+}  // namespace pa
+
+PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* context_lens, int num_seqs, int max_context_len,
+                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, float scale, int partition_size, void* workspace,
+                              size_t workspace_bytes, int dtype, int flags, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, flags,
+                     nullptr, stream);
 }

@@ -35,6 +35,7 @@ struct pa_pool {
   std::unordered_map<int64_t, Seq> seqs;
   int64_t copies = 0;
   int64_t tokens = 0;
+  int64_t shared = 0;  // blocks with refcount > 1
 
   int32_t alloc() {
     int32_t b = ring[head];
@@ -43,7 +44,11 @@ struct pa_pool {
     ref[b] = 1;
     return b;
   }
+  void retain(int32_t b) {
+    if (++ref[b] == 2) ++shared;
+  }
   void release(int32_t b) {
+    if (ref[b] == 2) --shared;
     if (--ref[b] == 0) {
       ring[(head + count) % num_blocks] = b;
       ++count;
@@ -133,7 +138,7 @@ PA_EXPORT pa_status pa_seq_fork(pa_pool* p, int64_t parent, int64_t child) {
   if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
   if (p->seqs.count(child)) return PA_ERR_INVALID;
   Seq c = it->second;  // copy before emplace (rehash may move it)
-  for (int32_t b : c.table) ++p->ref[b];
+  for (int32_t b : c.table) p->retain(b);
   p->tokens += c.fill;
   p->seqs.emplace(child, std::move(c));
   return PA_OK;
@@ -254,17 +259,20 @@ PA_EXPORT pa_status pa_pool_free_list(const pa_pool* p, int32_t* out, int cap, i
 
 PA_EXPORT pa_status pa_pool_stats(const pa_pool* p, int64_t* stats_out) {
   if (!p || !stats_out) return PA_ERR_INVALID;
-  int64_t used = 0, shared = 0;
-  for (int32_t r : p->ref) {
-    used += r > 0;
-    shared += r > 1;
-  }
+  int64_t used = 0;
+  for (int32_t r : p->ref) used += r > 0;
   stats_out[0] = p->count;
   stats_out[1] = used;
-  stats_out[2] = shared;
+  stats_out[2] = p->shared;
   stats_out[3] = p->tokens;
   stats_out[4] = p->copies;
   return PA_OK;
+}
+
+// Internal (not in the ABI): number of blocks currently held by more than one
+// sequence, O(1).
+extern "C" __attribute__((visibility("hidden"))) int64_t pa_pool_shared_blocks(const pa_pool* p) {
+  return p ? p->shared : 0;
 }
 
 PA_EXPORT size_t pa_kv_bytes_per_token(int num_layers, int num_kv_heads, int head_dim,
@@ -292,4 +300,4 @@ PA_EXPORT const char* pa_status_str(int status) {
   }
 }
 
-PA_EXPORT int pa_abi_version(void) { return 1; }
+PA_EXPORT int pa_abi_version(void) { return 2; }

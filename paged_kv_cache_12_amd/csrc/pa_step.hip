@@ -4,9 +4,13 @@
 // append, tables and lengths into one pinned staging buffer; device side: one
 // host-to-device copy, then copy-on-write copies, the block write and decode,
 // all on the caller's stream.
+#include <algorithm>
 #include <cstring>
+#include <numeric>
 
 #include "pa_internal.h"
+
+extern "C" int64_t pa_pool_shared_blocks(const pa_pool* p);
 
 namespace {
 
@@ -15,7 +19,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct StagingLayout {
-  size_t slots, pairs, lens, tables, total;
+  size_t slots, pairs, lens, order, tables, total;
 };
 
 StagingLayout staging_layout(int n, int maxb) {
@@ -23,7 +27,8 @@ StagingLayout staging_layout(int n, int maxb) {
   L.slots = 0;
   L.pairs = L.slots + align_up(sizeof(int64_t) * n);
   L.lens = L.pairs + align_up(sizeof(int32_t) * 2 * n);
-  L.tables = L.lens + align_up(sizeof(int32_t) * n);
+  L.order = L.lens + align_up(sizeof(int32_t) * n);
+  L.tables = L.order + align_up(sizeof(int32_t) * n);
   L.total = L.tables + align_up(sizeof(int32_t) * static_cast<size_t>(n) * maxb);
   return L;
 }
@@ -84,6 +89,7 @@ PA_EXPORT pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_s
   int64_t* h_slots = reinterpret_cast<int64_t*>(h + L.slots);
   int32_t* h_pairs = reinterpret_cast<int32_t*>(h + L.pairs);
   int32_t* h_lens = reinterpret_cast<int32_t*>(h + L.lens);
+  int32_t* h_order = reinterpret_cast<int32_t*>(h + L.order);
   int32_t* h_tab = reinterpret_cast<int32_t*>(h + L.tables);
 
   // 1. host pool: one new position per sequence (all-or-nothing)
@@ -95,6 +101,11 @@ PA_EXPORT pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_s
   if (st != PA_OK) return st;
   int max_ctx = 0;
   for (int i = 0; i < num_seqs; ++i) max_ctx = h_lens[i] > max_ctx ? h_lens[i] : max_ctx;
+  // longest contexts first, so that short work fills the end of the launch
+  std::iota(h_order, h_order + num_seqs, 0);
+  std::stable_sort(h_order, h_order + num_seqs,
+                   [h_lens](int32_t x, int32_t y) { return h_lens[x] > h_lens[y]; });
+  const int flags = pa_pool_shared_blocks(pool) > 0 ? PA_DECODE_SHARED_KV : 0;
 
   // 3. one host-to-device copy of slots, pairs, lengths and tables
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -109,8 +120,9 @@ PA_EXPORT pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_s
   st = pa_write_kv(k_new, v_new, k_cache, v_cache, reinterpret_cast<const int64_t*>(d + L.slots),
                    num_seqs, num_blocks, num_kv_heads, head_dim, block_size, dtype, stream);
   if (st != PA_OK) return st;
-  return pa_decode(out, q, k_cache, v_cache, reinterpret_cast<const int32_t*>(d + L.tables),
-                   max_blocks_per_seq, reinterpret_cast<const int32_t*>(d + L.lens), num_seqs,
-                   max_ctx, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
-                   partition_size, workspace, workspace_bytes, dtype, stream);
+  return decode_impl(out, q, k_cache, v_cache, reinterpret_cast<const int32_t*>(d + L.tables),
+                     max_blocks_per_seq, reinterpret_cast<const int32_t*>(d + L.lens), num_seqs,
+                     max_ctx, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     partition_size, workspace, workspace_bytes, dtype, flags,
+                     reinterpret_cast<const int32_t*>(d + L.order), stream);
 }

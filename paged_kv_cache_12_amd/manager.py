@@ -11,8 +11,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (Pool, PA_OK, PAError, pa_copy_blocks, pa_decode, pa_decode_workspace_size,
-               pa_write_kv)
+from . import (Pool, PA_OK, PA_DECODE_SHARED_KV, PAError, pa_copy_blocks, pa_decode,
+               pa_decode_workspace_size, pa_write_kv)
 
 TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
 
@@ -124,6 +124,7 @@ class PagedKVCache:
         need = pa_decode_workspace_size(q.shape[0], q.shape[1], self.d, max_ctx, partition_size)
         if need and (self._ws is None or self._ws.numel() < need):
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        flags = PA_DECODE_SHARED_KV if self.pool.stats()["shared"] > 0 else 0
         pa_decode(out, q, self.k_cache, self.v_cache, bt, ln, max_ctx, scale, partition_size,
-                  workspace=self._ws if need else None, stream=stream)
+                  workspace=self._ws if need else None, stream=stream, flags=flags)
         return out, tables, lens

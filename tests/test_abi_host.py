@@ -49,7 +49,7 @@ def test_status_strings(L):
     assert pa.status_str(0) == "ok"
     assert pa.status_str(3) == "not enough free blocks"
     assert pa.status_str(99) == "unknown status"
-    assert L.pa_abi_version() == 1
+    assert L.pa_abi_version() == 2
 
 
 def test_kv_bytes_per_token_matches_closed_form(L):
@@ -77,11 +77,11 @@ def test_workspace_size(L):
 def _decode(L, **kw):
     a = dict(out=16, q=16, kc=16, vc=16, bt=16, maxb=8, lens=16, B=2, max_ctx=100, H_q=8,
              H_kv=2, d=128, bs=16, nb=10, scale=0.1, part=512, ws=None, ws_bytes=0, dt=2,
-             stream=None)
+             flags=0, stream=None)
     a.update(kw)
     return L.pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["maxb"], a["lens"], a["B"],
                        a["max_ctx"], a["H_q"], a["H_kv"], a["d"], a["bs"], a["nb"], a["scale"],
-                       a["part"], a["ws"], a["ws_bytes"], a["dt"], a["stream"])
+                       a["part"], a["ws"], a["ws_bytes"], a["dt"], a["flags"], a["stream"])
 
 
 def test_decode_validation(L):
@@ -100,6 +100,7 @@ def test_decode_validation(L):
     assert _decode(L, B=0) == pa.PA_OK                 # nothing to do
     assert _decode(L, B=-1) == INV
     assert _decode(L, H_kv=0) == INV
+    assert _decode(L, flags=2) == INV                  # unknown flag
 
 
 def test_write_and_copy_validation(L):
@@ -267,4 +268,4 @@ def test_decode_step_rejects_before_touching_the_pool(L):
     full.append(0, 32)
     assert _step(L, full, [0]) == pa.PA_ERR_NO_BLOCKS
     assert (pool.free_list().tolist(), pool.stats()) == before
-    assert pa.pa_decode_step_staging_size(64, 257) == 512 + 512 + 256 + (64 * 257 * 4 + 255) // 256 * 256
+    assert pa.pa_decode_step_staging_size(64, 257) == 512 + 512 + 256 + 256 + (64 * 257 * 4 + 255) // 256 * 256
