@@ -146,6 +146,10 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  *        index >= ceil(context_lens[s] / block_size) are never read
  *   context_lens  device int32 [num_seqs]; must be <= max_context_len
  *        (larger values are clamped to it) and <= max_blocks_per_seq*block_size
+ *   seq_order  device int32 [num_seqs] or NULL: the order in which sequences
+ *        are issued to the GPU (a permutation of 0..num_seqs-1; longest first
+ *        balances the launch).  A scheduling hint: results do not depend on it;
+ *        entries outside [0, num_seqs) are skipped
  *   scale  softmax scale (1/sqrt(head_dim) for standard attention)
  *   partition_size  0: one work unit per (sequence, KV head); otherwise the
  *        context is split into partitions of this many tokens (a multiple of
@@ -163,7 +167,8 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  */
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, int max_blocks_per_seq,
-                    const int32_t* context_lens, int num_seqs, int max_context_len,
+                    const int32_t* context_lens, const int32_t* seq_order, int num_seqs,
+                    int max_context_len,
                     int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                     int num_blocks, float scale, int partition_size, void* workspace,
                     size_t workspace_bytes, int dtype, int flags, void* stream);
@@ -180,8 +185,10 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * decode issues the longest contexts first and sets PA_DECODE_SHARED_KV
  * itself whenever the pool holds a block with refcount > 1.
  *
- *   host_staging  pinned host memory, >= pa_decode_step_staging_size() bytes,
- *                 16-byte aligned; read by the asynchronous copy, so it must
+ *   host_staging  pinned host memory (hipHostMalloc), >=
+ *                 pa_decode_step_staging_size() bytes, 16-byte aligned; a
+ *                 small kernel on `stream` reads it through its device
+ *                 mapping (an asynchronous copy if it has none), so it must
  *                 not be rewritten until the stream has passed this call
  *                 (alternate two buffers and wait on an event)
  *   dev_staging   device memory of the same size; holds the step's metadata

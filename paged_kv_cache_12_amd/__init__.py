@@ -35,8 +35,8 @@ SIGNATURES = {
     "pa_write_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "pa_copy_blocks": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "pa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
-    "pa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i,
-                       _vp, _sz, _i, _i, _vp]),
+    "pa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
+                       _i, _vp, _sz, _i, _i, _vp]),
     "pa_decode_step_staging_size": (_sz, [_i, _i]),
     "pa_decode_step": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _f,
                             _i, _i, _vp, _vp, _sz, _vp, _sz, _i, _vp]),
@@ -181,8 +181,9 @@ def pa_decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int,
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
               scale: float, partition_size: int = 512, workspace=None, stream=None,
-              flags: int = 0):
-    """out, q [B][H_q][d]; block_tables int32 [B][maxb]; context_lens int32 [B]."""
+              flags: int = 0, seq_order=None):
+    """out, q [B][H_q][d]; block_tables int32 [B][maxb]; context_lens int32 [B];
+    seq_order: optional int32 GPU tensor [B] (issue order of the sequences)."""
     torch = _torch()
     nb, H_kv, bs, d = cache_geometry(k_cache, v_cache)
     B, H_q, dq = q.shape
@@ -200,9 +201,14 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
         if workspace.numel() * workspace.element_size() < need:
             raise ValueError("workspace too small")
         ws_ptr, ws_bytes = _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    order_ptr = None
+    if seq_order is not None:
+        if seq_order.dtype != torch.int32 or seq_order.numel() != B:
+            raise ValueError("seq_order must be int32 [B]")
+        order_ptr = _dev_ptr(seq_order, "seq_order")
     st = lib().pa_decode(_dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
                          _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables"),
-                         block_tables.shape[1], _dev_ptr(context_lens, "context_lens"), B,
+                         block_tables.shape[1], _dev_ptr(context_lens, "context_lens"), order_ptr, B,
                          max_context_len, H_q, H_kv, d, bs, nb, float(scale), partition_size,
                          ws_ptr, ws_bytes, torch_dtype_code(q), flags, _stream_ptr(stream))
     _check(st, "pa_decode")

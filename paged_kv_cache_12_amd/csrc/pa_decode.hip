@@ -833,12 +833,13 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
 
 PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_tables, int max_blocks_per_seq,
-                              const int32_t* context_lens, int num_seqs, int max_context_len,
-                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                              int num_blocks, float scale, int partition_size, void* workspace,
-                              size_t workspace_bytes, int dtype, int flags, void* stream) {
+                              const int32_t* context_lens, const int32_t* seq_order, int num_seqs,
+                              int max_context_len, int num_q_heads, int num_kv_heads,
+                              int head_dim, int block_size, int num_blocks, float scale,
+                              int partition_size, void* workspace, size_t workspace_bytes,
+                              int dtype, int flags, void* stream) {
   return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, flags,
-                     nullptr, stream);
+                     seq_order, stream);
 }

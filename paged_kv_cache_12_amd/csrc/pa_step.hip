@@ -33,6 +33,16 @@ StagingLayout staging_layout(int n, int maxb) {
   return L;
 }
 
+// Copies the pinned host staging buffer into device memory from a kernel on
+// the caller's stream: the compute queue does not wait on a copy engine.
+// System-scope loads always see what the host wrote before the launch.
+__global__ __launch_bounds__(256) void stage_copy_kernel(const uint64_t* __restrict__ src,
+                                                         uint64_t* __restrict__ dst, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 }  // namespace
 
 using namespace pa;
@@ -107,9 +117,21 @@ PA_EXPORT pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_s
                    [h_lens](int32_t x, int32_t y) { return h_lens[x] > h_lens[y]; });
   const int flags = pa_pool_shared_blocks(pool) > 0 ? PA_DECODE_SHARED_KV : 0;
 
-  // 3. one host-to-device copy of slots, pairs, lengths and tables
+  // 3. one host-to-device copy of slots, pairs, lengths, order and tables:
+  //    a copy kernel reading the pinned buffer when it is mapped on the device,
+  //    else an asynchronous copy
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(d, h, L.total, hipMemcpyHostToDevice, s) != hipSuccess) return PA_ERR_HIP;
+  void* h_dev = nullptr;
+  if (hipHostGetDevicePointer(&h_dev, host_staging, 0) == hipSuccess && h_dev) {
+    const int64_t n = static_cast<int64_t>(L.total / sizeof(uint64_t));
+    const int blocks = static_cast<int>((n + 255) / 256 < 64 ? (n + 255) / 256 : 64);
+    hipLaunchKernelGGL(stage_copy_kernel, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const uint64_t*>(h_dev), reinterpret_cast<uint64_t*>(d), n);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  } else {
+    (void)hipGetLastError();
+    if (hipMemcpyAsync(d, h, L.total, hipMemcpyHostToDevice, s) != hipSuccess) return PA_ERR_HIP;
+  }
 
   // 4. copy-on-write, block write, decode
   if (npairs > 0) {

@@ -79,7 +79,7 @@ def _decode(L, **kw):
              H_kv=2, d=128, bs=16, nb=10, scale=0.1, part=512, ws=None, ws_bytes=0, dt=2,
              flags=0, stream=None)
     a.update(kw)
-    return L.pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["maxb"], a["lens"], a["B"],
+    return L.pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["maxb"], a["lens"], None, a["B"],
                        a["max_ctx"], a["H_q"], a["H_kv"], a["d"], a["bs"], a["nb"], a["scale"],
                        a["part"], a["ws"], a["ws_bytes"], a["dt"], a["flags"], a["stream"])
 

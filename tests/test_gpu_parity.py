@@ -310,7 +310,7 @@ def test_decode_step_matches_oracle(dtype, part):
     ds = torch.empty(sbytes, dtype=torch.uint8, device="cuda")
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
     rng = np.random.default_rng(3)
-    for step in range(3):
+    for step in range(8):
         kn = synth.cast_storage(rng.standard_normal((B, H_kv, d), dtype=np.float32), dtype)
         vn = synth.cast_storage(rng.standard_normal((B, H_kv, d), dtype=np.float32), dtype)
         q = synth.cast_storage(rng.standard_normal((B, H_q, d), dtype=np.float32), dtype)
@@ -330,3 +330,32 @@ def test_decode_step_matches_oracle(dtype, part):
         got = to_f64(out, dtype)
         H.check_attention(got, ref, dtype, range(B))
     assert_caches_equal(gs, os_)
+
+
+@pytest.mark.parametrize("part", [0, 64])
+def test_seq_order_is_only_a_schedule(part):
+    import torch
+    import paged_kv_cache_12_amd as pa
+    from paged_kv_cache_12_amd.manager import storage_to_torch
+    say("seq_order", part)
+    sc = small_scenario("bf16", 32, 8, 128, 16, seed=777 + part)
+    gs = H.GpuSide(sc)
+    H.execute(sc, gs)
+    tab, lens = gs.cache.tables(sc.decode_seqs)
+    bt = torch.from_numpy(tab).cuda()
+    ln = torch.from_numpy(lens).cuda()
+    q = storage_to_torch(sc.q, "bf16").cuda()
+    ws = torch.zeros(max(256, pa.pa_decode_workspace_size(len(sc.decode_seqs), 32, 128,
+                                                          int(lens.max()), part)),
+                     dtype=torch.uint8, device="cuda")
+    outs = []
+    B = len(sc.decode_seqs)
+    for order in (None, np.arange(B)[::-1], np.random.default_rng(1).permutation(B)):
+        o = torch.empty_like(q)
+        so = None if order is None else torch.from_numpy(np.ascontiguousarray(order, dtype=np.int32)).cuda()
+        pa.pa_decode(o, q, gs.cache.k_cache, gs.cache.v_cache, bt, ln, int(lens.max()), sc.wl.scale,
+                     part, workspace=ws, seq_order=so)
+        outs.append(o)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
