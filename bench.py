@@ -9,7 +9,11 @@ attention output.  Inputs are resident in HBM before the timed region starts.
 
 Prints one JSON line.  `value` is the effective KV bandwidth of the whole step
 (algorithmic KV bytes read by the step's decode / step time);
-`roofline` covers pa_decode alone, timed with HIP events on its stream.
+`roofline` covers pa_decode alone, timed with HIP events on its stream, cache
+cold (the calls cycle through copies of the caches, one per layer, so that
+more KV than the L2s and the MALL hold is read between two reads of one
+copy), mean of the calls.
+The oracle baseline runs first, in processes forked before any GPU use.
 """
 from __future__ import annotations
 
@@ -42,6 +46,8 @@ def parse():
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-workers", type=int, default=None,
+                    help="processes for the oracle baseline (default: host cores, <= 16)")
     ap.add_argument("--calibrate", action="store_true",
                     help="run only a 1 GiB device copy and fill of known size (for scaling "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -118,16 +124,42 @@ def unique_kv_bytes(tables, lens, wl):
     return float(sum(seen.values())) * 2 * wl.h_kv * wl.head_dim * synth.ELEM_BYTES[wl.dtype]
 
 
-def cpu_baseline(sc, budget_s: float):
-    """Time the oracle (as it stands) on a bounded sample of the same workload:
-    its pool model and cache writes set up the sample, then paged_decode over
-    the sample's sequences is repeated until `budget_s` seconds have passed."""
+def host_cores() -> int:
+    """Host cores this process may use (the box gives one GPU 16 of them)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+_SAMPLE = {}
+
+
+def _oracle_rows(rows):
+    """Worker body: the oracle's paged_decode on some rows of the sample."""
+    from oracle import attention as A
+    t = _SAMPLE
+    A.paged_decode(t["q"], t["kc"], t["vc"], t["tab"], t["lens"], t["scale"], t["dtype"],
+                   seqs=rows)
+    return len(rows)
+
+
+def cpu_baseline(sc, budget_s: float, workers: int):
+    """Time the oracle (as it stands) on a bounded sample of the same workload.
+
+    Its pool model and cache writes set up the sample; then paged_decode over
+    the sample's sequences is repeated until `budget_s` seconds have passed.
+    The sequences are spread over `workers` forked processes (one BLAS thread
+    each), which inherit the sample copy-on-write.  Must run before this
+    process touches the GPU: the workers are forked, not started afresh."""
+    import multiprocessing as mp
     from threadpoolctl import threadpool_limits
     from oracle import attention as A
     from oracle.pool_model import PoolModel
     wl = sc.wl
     B = len(sc.decode_seqs)
-    nsamp = min(B, 8)
+    nsamp = min(B, max(8, 2 * workers))
     samp = sc.decode_seqs[:nsamp]
     model = PoolModel(sc.num_blocks, wl.block_size, sc.free_order)
     st = synth.STORAGE[wl.dtype]
@@ -146,23 +178,32 @@ def cpu_baseline(sc, budget_s: float):
     lens = np.array([n for _, n in tabs], np.int32)
     for i, (t, _) in enumerate(tabs):
         tab[i, :len(t)] = t
-    q = sc.q[:nsamp]
     kv_bytes = float(lens.sum()) * 2 * wl.h_kv * wl.head_dim * synth.ELEM_BYTES[wl.dtype]
+    _SAMPLE.update(q=sc.q[:nsamp], kc=kc, vc=vc, tab=tab, lens=lens, scale=wl.scale,
+                   dtype=wl.dtype)
+    # longest first, dealt round-robin so the workers get similar work
+    order = [int(i) for i in np.argsort(-lens, kind="stable")]
+    chunks = [order[w::workers] for w in range(workers) if order[w::workers]]
     reps = 0
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            A.paged_decode(q, kc, vc, tab, lens, wl.scale, wl.dtype)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s:
-                break
+        with mp.get_context("fork").Pool(len(chunks)) as pool:
+            pool.map(_oracle_rows, [[r] for r in order[:len(chunks)]])   # workers up
+            t0 = time.perf_counter()
+            while True:
+                done = sum(pool.map(_oracle_rows, chunks, chunksize=1))
+                assert done == nsamp
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= budget_s:
+                    break
+    _SAMPLE.clear()
     per_step = el / reps
-    return {"value": kv_bytes / per_step / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": kv_bytes / per_step / 1e9, "unit": "GB/s", "cores": len(chunks),
+            "kind": "oracle",
             "seq_steps_per_s": nsamp / per_step,
             "sample": f"{nsamp} of {B} sequences of {wl.name} (ctx {int(lens.min())}-"
-                      f"{int(lens.max())}), fp64 NumPy paged_decode repeated {reps}x over "
-                      f"{el:.1f} s, BLAS limited to 1 thread"}
+                      f"{int(lens.max())}), fp64 NumPy paged_decode in {len(chunks)} "
+                      f"processes x 1 BLAS thread, repeated {reps}x over {el:.1f} s"}
 
 
 def main():
@@ -174,14 +215,17 @@ def main():
     if args.calibrate:
         calibrate()
         return
+    wl = synth.WORKLOADS[args.workload]
+    part = wl.partition if args.partition is None else args.partition
+    sc = synth.build_scenario(wl)
+    # the oracle on the host first: its workers are forked before any GPU use
+    cpu = None if args.no_cpu_baseline else cpu_baseline(
+        sc, args.cpu_seconds, args.cpu_workers or host_cores())
     import torch
     import paged_kv_cache_12_amd as pa
     from paged_kv_cache_12_amd.manager import PagedKVCache, storage_to_torch
     pa.lib()
     dev = torch.device("cuda:0")
-    wl = synth.WORKLOADS[args.workload]
-    part = wl.partition if args.partition is None else args.partition
-    sc = synth.build_scenario(wl)
     cache = PagedKVCache(sc.num_blocks, wl.block_size, wl.h_kv, wl.head_dim, wl.dtype,
                          device=dev, free_order=sc.free_order)
     fill_cache(sc, cache, dev)
@@ -201,6 +245,7 @@ def main():
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     step_bytes = []
+    host_s = []
     # aliased blocks (forks, shared prefixes): cached loads
     flags = pa.PA_DECODE_SHARED_KV if cache.pool.stats()["shared"] > 0 else 0
 
@@ -219,8 +264,10 @@ def main():
             j = i & 1
             if done[j] is not None:
                 done[j].synchronize()      # staging buffer j is free again
+            h0 = time.perf_counter()
             pa.pa_decode_step(cache.pool, seqs, step_k, step_v, cache.k_cache, cache.v_cache,
                               q, out, wl.scale, part, maxb, h_stage[j], d_stage, ws)
+            host_s.append(time.perf_counter() - h0)
             ev = torch.cuda.Event()
             ev.record(stream)
             done[j] = ev
@@ -231,10 +278,13 @@ def main():
         d_len = torch.from_numpy(len_h).to(dev)
         max_ctx0 = int(len_h.max())
         kv0 = float(len_h.sum()) * 2 * wl.h_kv * wl.head_dim * e
+        order0 = torch.from_numpy(pa.pa_decode_order(tab_h, len_h)).to(dev)
 
         def step(i):
+            h0 = time.perf_counter()
             pa.pa_decode(out, q, cache.k_cache, cache.v_cache, d_tab, d_len, max_ctx0,
-                         wl.scale, part, workspace=ws, flags=flags)
+                         wl.scale, part, workspace=ws, flags=flags, seq_order=order0)
+            host_s.append(time.perf_counter() - h0)
             step_bytes.append(kv0)
 
     for i in range(args.warmup):
@@ -248,31 +298,86 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     kv_step = float(np.mean(step_bytes[args.warmup:]))
     value = kv_step / (ms_step * 1e-3) / 1e9
+    hs = np.array(host_s[args.warmup:]) * 1e6
+    host_us = {"median": round(float(np.median(hs)), 2),
+               "p90": round(float(np.percentile(hs, 90)), 2),
+               "what": "host time of the step's native call (pool append, staging, launches)"
+               if appends else "host time of the pa_decode call (launch)"}
 
     # the dominant kernel: pa_decode alone on the final tables, HIP events on
-    # its stream
+    # its stream.  Cache cold as in a multi-layer decode: the calls cycle
+    # through `nrot` copies of the caches (one per layer), so that at least
+    # 1 GiB of other KV is read between two reads of one copy (more than the
+    # L2s and the MALL hold).  One event pair brackets the timed calls (their
+    # average duration); then per-call events (spread) and the same calls on
+    # one copy (warm), as diagnostics.
     tab_h, len_h = cache.tables(seqs, maxb)
     d_tab = torch.from_numpy(tab_h).to(dev)
     d_len = torch.from_numpy(len_h).to(dev)
-    # the issue order pa_decode_step uses: longest contexts first
-    d_order = torch.from_numpy(np.argsort(-len_h, kind="stable").astype(np.int32)).to(dev)
+    # the issue order pa_decode_step uses
+    d_order = torch.from_numpy(pa.pa_decode_order(tab_h, len_h)).to(dev)
     max_ctx = int(len_h.max())
     kv_dec = float(len_h.sum()) * 2 * wl.h_kv * wl.head_dim * e
+    unique = unique_kv_bytes(tab_h, len_h, wl)
+    nrot = 1 + math.ceil((1 << 30) / unique)
+    copies = [(cache.k_cache, cache.v_cache)] + [
+        (cache.k_cache.clone(), cache.v_cache.clone()) for _ in range(nrot - 1)]
+
+    def decode(i):
+        kc, vc = copies[i % nrot]
+        pa.pa_decode(out, q, kc, vc, d_tab, d_len, max_ctx, wl.scale, part,
+                     workspace=ws, flags=flags, seq_order=d_order)
+
+    def bracketed(n, rotate):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            decode(i if rotate else 0)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for i in range(2 * nrot):
+        decode(i)
+    torch.cuda.synchronize()
+    dec_ms = bracketed(args.steps, True)         # average launch duration, cache cold
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    for _ in range(3):
-        pa.pa_decode(out, q, cache.k_cache, cache.v_cache, d_tab, d_len, max_ctx, wl.scale, part,
-                     workspace=ws, flags=flags, seq_order=d_order)
-    for a0, a1 in evs:
+    for i, (a0, a1) in enumerate(evs):
         a0.record(stream)
-        pa.pa_decode(out, q, cache.k_cache, cache.v_cache, d_tab, d_len, max_ctx, wl.scale, part,
-                     workspace=ws, flags=flags, seq_order=d_order)
+        decode(i)
         a1.record(stream)
     torch.cuda.synchronize()
-    dec_ms_mean = float(np.mean([a0.elapsed_time(a1) for a0, a1 in evs]))
-    achieved = kv_dec / (dec_ms_mean * 1e-3) / 1e9
-    unique = unique_kv_bytes(tab_h, len_h, wl)
-    unique_rate = unique / (dec_ms_mean * 1e-3) / 1e9
+    per_call = np.array([a0.elapsed_time(a1) for a0, a1 in evs])
+    warm_ms = bracketed(args.steps, False)
+    achieved = kv_dec / (dec_ms * 1e-3) / 1e9
+    unique_rate = unique / (dec_ms * 1e-3) / 1e9
+
+    # pa_copy_blocks at this workload's shapes: as many pairs as the fill made
+    # copy-on-write copies (at least 64), from used blocks into free ones (the
+    # decode above never reads a free block), cycling through the copies
+    copy = None
+    free = cache.pool.free_list()
+    used = np.unique(tab_h[tab_h >= 0])
+    npairs = min(max(int(cache.pool.stats()["copies"]), 64), free.size, used.size)
+    if npairs > 0:
+        pairs = np.stack([used[:npairs], free[:npairs]], axis=1).astype(np.int32)
+        d_pairs = torch.from_numpy(pairs).to(dev)
+        ncopy = 20
+        for i in range(nrot):
+            pa.pa_copy_blocks(copies[i][0], copies[i][1], d_pairs)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(ncopy):
+            pa.pa_copy_blocks(copies[i % nrot][0], copies[i % nrot][1], d_pairs)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        c_ms = e0.elapsed_time(e1) / ncopy
+        c_bytes = npairs * 2 * 2 * wl.h_kv * wl.block_size * wl.head_dim * e
+        copy = {"pairs": npairs, "us_mean": round(c_ms * 1e3, 2),
+                "bytes_read_plus_written": c_bytes,
+                "GBps": round(c_bytes / (c_ms * 1e-3) / 1e9, 1)}
+    del copies
 
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
@@ -301,7 +406,14 @@ def main():
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(B / (ms_step * 1e-3), 1),
-        "decode_ms_mean": round(dec_ms_mean, 5),
+        "decode_ms_mean": round(dec_ms, 5),
+        "decode_cold_copies": nrot,
+        "decode_ms_per_call_p10_median_p90": [round(float(np.percentile(per_call, x)), 5)
+                                              for x in (10, 50, 90)],
+        "decode_warm_ms_mean": round(warm_ms, 5),
+        "warm_achieved": round(unique / (warm_ms * 1e-3) / 1e9, 1),
+        "host_us_per_step": host_us,
+        "copy_blocks": copy,
         # HBM roofline on the bytes HBM must deliver: each physical block once
         # (equal to the logical bytes unless sequences share blocks)
         "roofline": {"bound": "hbm", "achieved": round(unique_rate, 1), "peak": HBM_PEAK_GBS,
@@ -313,8 +425,8 @@ def main():
                      "logical_bytes_per_launch": round(kv_dec),
                      "logical_achieved": round(achieved, 1)},
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(sc, args.cpu_seconds)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

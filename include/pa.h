@@ -147,9 +147,9 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  *   context_lens  device int32 [num_seqs]; must be <= max_context_len
  *        (larger values are clamped to it) and <= max_blocks_per_seq*block_size
  *   seq_order  device int32 [num_seqs] or NULL: the order in which sequences
- *        are issued to the GPU (a permutation of 0..num_seqs-1; longest first
- *        balances the launch).  A scheduling hint: results do not depend on it;
- *        entries outside [0, num_seqs) are skipped
+ *        are issued to the GPU (a permutation of 0..num_seqs-1, for example
+ *        from pa_decode_order).  A scheduling hint: results do not depend on
+ *        it; entries outside [0, num_seqs) are skipped
  *   scale  softmax scale (1/sqrt(head_dim) for standard attention)
  *   partition_size  0: one work unit per (sequence, KV head); otherwise the
  *        context is split into partitions of this many tokens (a multiple of
@@ -174,6 +174,25 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     size_t workspace_bytes, int dtype, int flags, void* stream);
 
 /*
+ * pa_decode_order — the issue order pa_decode_step gives pa_decode (host
+ * memory only; no HIP calls).  Sequences whose tables start with the same
+ * physical block (forks, shared prefixes) form a group; groups come in
+ * decreasing order of their longest context (first appearance breaks ties)
+ * and, inside a group, sequences in decreasing context length (index breaks
+ * ties).  Keeping sharers together lets a shared block be read from the
+ * caches while it is still there; longest first keeps long work from ending
+ * the launch.
+ *
+ *   block_tables  host int32 [num_seqs][max_blocks_per_seq] (entry 0 read
+ *                 when context_lens[s] > 0)
+ *   context_lens  host int32 [num_seqs]
+ *   order_out     host int32 [num_seqs]: a permutation of 0..num_seqs-1
+ * PA_ERR_INVALID for negative sizes or a null pointer when num_seqs > 0.
+ */
+pa_status pa_decode_order(const int32_t* block_tables, int max_blocks_per_seq,
+                          const int32_t* context_lens, int num_seqs, int32_t* order_out);
+
+/*
  * pa_decode_step — one decode iteration of a batch as the central manager
  * hands it to the GPU (encyclopedia entry, "como funciona": the manager ships
  * the block tables with each iteration's input): append one position to each
@@ -182,8 +201,9 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * asynchronous host-to-device copy, then run pa_copy_blocks (if any pair),
  * pa_write_kv of k_new / v_new (device [num_seqs][H_kv][d]) into the new
  * positions, and pa_decode of q into out (device [num_seqs][H_q][d]).  The
- * decode issues the longest contexts first and sets PA_DECODE_SHARED_KV
- * itself whenever the pool holds a block with refcount > 1.
+ * decode issues the sequences in pa_decode_order's order and sets
+ * PA_DECODE_SHARED_KV itself whenever the pool holds a block with
+ * refcount > 1.
  *
  *   host_staging  pinned host memory (hipHostMalloc), >=
  *                 pa_decode_step_staging_size() bytes, 16-byte aligned; a

@@ -37,6 +37,7 @@ SIGNATURES = {
     "pa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "pa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                        _i, _vp, _sz, _i, _i, _vp]),
+    "pa_decode_order": (_i, [_vp, _i, _vp, _i, _vp]),
     "pa_decode_step_staging_size": (_sz, [_i, _i]),
     "pa_decode_step": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _f,
                             _i, _i, _vp, _vp, _sz, _vp, _sz, _i, _vp]),
@@ -213,6 +214,20 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
                          ws_ptr, ws_bytes, torch_dtype_code(q), flags, _stream_ptr(stream))
     _check(st, "pa_decode")
     return workspace
+
+
+def pa_decode_order(block_tables: np.ndarray, context_lens: np.ndarray) -> np.ndarray:
+    """Issue order for pa_decode from host tables int32 [B][maxb] and lengths
+    int32 [B]: sharers of a first block together, longest work first."""
+    tab = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B = lens.size
+    if tab.ndim != 2 or tab.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    out = np.empty(B, dtype=np.int32)
+    _check(lib().pa_decode_order(_np_ptr(tab), tab.shape[1], _np_ptr(lens), B, _np_ptr(out)),
+           "pa_decode_order")
+    return out
 
 
 def pa_decode_step_staging_size(num_seqs: int, max_blocks_per_seq: int) -> int:

@@ -275,6 +275,48 @@ extern "C" __attribute__((visibility("hidden"))) int64_t pa_pool_shared_blocks(c
   return p ? p->shared : 0;
 }
 
+PA_EXPORT pa_status pa_decode_order(const int32_t* block_tables, int max_blocks_per_seq,
+                                    const int32_t* context_lens, int num_seqs,
+                                    int32_t* order_out) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0) return PA_ERR_INVALID;
+  if (num_seqs == 0) return PA_OK;
+  if (!block_tables || !context_lens || !order_out) return PA_ERR_INVALID;
+  // group = sequences whose table starts with the same physical block (a fork
+  // or a shared prefix always shares from the first block); an empty
+  // sequence or one without a first block is a group of its own
+  std::vector<int32_t> group(num_seqs), gmax;
+  std::unordered_map<int32_t, int32_t> first;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int32_t b0 = block_tables[static_cast<size_t>(s) * max_blocks_per_seq];
+    const int32_t len = context_lens[s];
+    int32_t g;
+    if (len > 0 && max_blocks_per_seq > 0 && b0 >= 0) {
+      auto it = first.find(b0);
+      if (it == first.end()) {
+        g = static_cast<int32_t>(gmax.size());
+        first.emplace(b0, g);
+        gmax.push_back(len);
+      } else {
+        g = it->second;
+        gmax[g] = std::max(gmax[g], len);
+      }
+    } else {
+      g = static_cast<int32_t>(gmax.size());
+      gmax.push_back(len);
+    }
+    group[s] = g;
+  }
+  for (int s = 0; s < num_seqs; ++s) order_out[s] = s;
+  std::sort(order_out, order_out + num_seqs, [&](int32_t x, int32_t y) {
+    const int32_t gx = group[x], gy = group[y];
+    if (gmax[gx] != gmax[gy]) return gmax[gx] > gmax[gy];
+    if (gx != gy) return gx < gy;
+    if (context_lens[x] != context_lens[y]) return context_lens[x] > context_lens[y];
+    return x < y;
+  });
+  return PA_OK;
+}
+
 PA_EXPORT size_t pa_kv_bytes_per_token(int num_layers, int num_kv_heads, int head_dim,
                                        int dtype) {
   size_t e;
@@ -300,4 +342,4 @@ PA_EXPORT const char* pa_status_str(int status) {
   }
 }
 
-PA_EXPORT int pa_abi_version(void) { return 2; }
+PA_EXPORT int pa_abi_version(void) { return 3; }

@@ -111,10 +111,9 @@ PA_EXPORT pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_s
   if (st != PA_OK) return st;
   int max_ctx = 0;
   for (int i = 0; i < num_seqs; ++i) max_ctx = h_lens[i] > max_ctx ? h_lens[i] : max_ctx;
-  // longest contexts first, so that short work fills the end of the launch
-  std::iota(h_order, h_order + num_seqs, 0);
-  std::stable_sort(h_order, h_order + num_seqs,
-                   [h_lens](int32_t x, int32_t y) { return h_lens[x] > h_lens[y]; });
+  // sharers together, longest work first
+  st = pa_decode_order(h_tab, max_blocks_per_seq, h_lens, num_seqs, h_order);
+  if (st != PA_OK) return st;
   const int flags = pa_pool_shared_blocks(pool) > 0 ? PA_DECODE_SHARED_KV : 0;
 
   // 3. one host-to-device copy of slots, pairs, lengths, order and tables:

@@ -12,7 +12,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import (Pool, PA_OK, PA_DECODE_SHARED_KV, PAError, pa_copy_blocks, pa_decode,
-               pa_decode_workspace_size, pa_write_kv)
+               pa_decode_order, pa_decode_workspace_size, pa_write_kv)
 
 TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
 
@@ -125,6 +125,8 @@ class PagedKVCache:
         if need and (self._ws is None or self._ws.numel() < need):
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         flags = PA_DECODE_SHARED_KV if self.pool.stats()["shared"] > 0 else 0
+        order = torch.from_numpy(pa_decode_order(tables, lens)).to(self.device)
         pa_decode(out, q, self.k_cache, self.v_cache, bt, ln, max_ctx, scale, partition_size,
-                  workspace=self._ws if need else None, stream=stream, flags=flags)
+                  workspace=self._ws if need else None, stream=stream, flags=flags,
+                  seq_order=order)
         return out, tables, lens

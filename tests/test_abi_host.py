@@ -33,7 +33,7 @@ def L():
 
 def test_library_exports_exactly_the_header_functions(L):
     declared = header_functions()
-    assert len(declared) == 21
+    assert len(declared) == 22
     for name in declared:
         assert hasattr(L, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
@@ -49,7 +49,7 @@ def test_status_strings(L):
     assert pa.status_str(0) == "ok"
     assert pa.status_str(3) == "not enough free blocks"
     assert pa.status_str(99) == "unknown status"
-    assert L.pa_abi_version() == 2
+    assert L.pa_abi_version() == 3
 
 
 def test_kv_bytes_per_token_matches_closed_form(L):
@@ -269,3 +269,49 @@ def test_decode_step_rejects_before_touching_the_pool(L):
     assert _step(L, full, [0]) == pa.PA_ERR_NO_BLOCKS
     assert (pool.free_list().tolist(), pool.stats()) == before
     assert pa.pa_decode_step_staging_size(64, 257) == 512 + 512 + 256 + 256 + (64 * 257 * 4 + 255) // 256 * 256
+
+
+def _order_by_definition(tab, lens):
+    """The documented issue order, written out: groups of sequences with the
+    same first physical block, groups by decreasing longest member (first
+    appearance breaks ties), members by decreasing length (index breaks ties)."""
+    B = len(lens)
+    key = []
+    for s in range(B):
+        key.append(int(tab[s][0]) if lens[s] > 0 and tab.shape[1] > 0 and tab[s][0] >= 0
+                   else ("solo", s))
+    first_seen, gmax = {}, {}
+    for s in range(B):
+        first_seen.setdefault(key[s], s)
+        gmax[key[s]] = max(gmax.get(key[s], lens[s]), lens[s])
+    return sorted(range(B), key=lambda s: (-gmax[key[s]], first_seen[key[s]], -lens[s], s))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_order_groups_sharers_longest_first(L, seed):
+    rng = np.random.default_rng(seed)
+    B, maxb = int(rng.integers(1, 80)), 8
+    tab = np.full((B, maxb), -1, np.int32)
+    lens = rng.integers(0, maxb * 16 + 1, B).astype(np.int32)
+    heads = rng.integers(0, max(1, B // 3), B)     # sharers of a few first blocks
+    for s in range(B):
+        nb = -(-int(lens[s]) // 16)
+        tab[s, :nb] = rng.integers(1000, 2000, nb)
+        if nb:
+            tab[s, 0] = heads[s]
+    got = pa.pa_decode_order(tab, lens)
+    assert sorted(got.tolist()) == list(range(B))
+    assert got.tolist() == _order_by_definition(tab, lens)
+    # sharers sit next to each other
+    firsts = [int(tab[s, 0]) for s in got if lens[s] > 0]
+    runs = [f for i, f in enumerate(firsts) if i == 0 or f != firsts[i - 1]]
+    assert len(runs) == len(set(runs))
+
+
+def test_decode_order_without_sharing_is_longest_first(L):
+    lens = np.array([5, 40, 40, 0, 17, 99], np.int32)
+    tab = np.arange(6, dtype=np.int32).reshape(6, 1)
+    assert pa.pa_decode_order(tab, lens).tolist() == [5, 1, 2, 4, 0, 3]
+    assert pa.pa_decode_order(np.zeros((0, 1), np.int32), np.zeros(0, np.int32)).size == 0
+    assert L.pa_decode_order(None, 1, None, 2, None) == pa.PA_ERR_INVALID
+    assert L.pa_decode_order(None, 1, None, -1, None) == pa.PA_ERR_INVALID
