@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cpu-workers", type=int, default=None,
                     help="processes for the oracle baseline (default: host cores, <= 16)")
+    ap.add_argument("--swap", action="store_true",
+                    help="measure swapping half of the workload's sequences out to pinned "
+                         "host memory and back (pa_seq_swap_out/in + pa_swap_blocks)")
     ap.add_argument("--calibrate", action="store_true",
                     help="run only a 1 GiB device copy and fill of known size (for scaling "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -206,6 +209,107 @@ def cpu_baseline(sc, budget_s: float, workers: int):
                       f"processes x 1 BLAS thread, repeated {reps}x over {el:.1f} s"}
 
 
+HOST_LINK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def bench_swap(args):
+    """Swap half of the workload's sequences out to pinned host blocks and back,
+    `steps` times; GB/s of block bytes per direction against the host link."""
+    import torch
+    import paged_kv_cache_12_amd as pa
+    from oracle import attention as A
+    from paged_kv_cache_12_amd.manager import PagedKVCache
+    wl = synth.WORKLOADS[args.workload]
+    sc = synth.build_scenario(wl)
+    dev = torch.device("cuda:0")
+    cache = PagedKVCache(sc.num_blocks, wl.block_size, wl.h_kv, wl.head_dim, wl.dtype,
+                         device=dev, free_order=sc.free_order)
+    fill_cache(sc, cache, dev)
+    cache.enable_swap(sc.num_blocks)
+    seqs = list(sc.decode_seqs)
+    out_set = seqs[: len(seqs) // 2]
+    e = synth.ELEM_BYTES[wl.dtype]
+    block_bytes = 2 * wl.h_kv * wl.block_size * wl.head_dim * e
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        cache.swap_out(out_set)
+        cache.swap_in(out_set)
+    torch.cuda.synchronize()
+    t_out, t_in, host_out, host_in, npairs = [], [], [], [], 0
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        h0 = time.perf_counter()
+        pairs = cache.swap_out(out_set)
+        h1 = time.perf_counter()
+        ev[1].record(stream)
+        h2 = time.perf_counter()
+        cache.swap_in(out_set)
+        h3 = time.perf_counter()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        npairs = len(pairs)
+        t_out.append(ev[0].elapsed_time(ev[1]))
+        t_in.append(ev[1].elapsed_time(ev[2]))
+        host_out.append((h1 - h0) * 1e6)
+        host_in.append((h3 - h2) * 1e6)
+    nbytes = npairs * block_bytes
+    # the same bytes as one contiguous copy each way (copy engines)
+    flat_d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    flat_h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    for _ in range(2):
+        flat_h.copy_(flat_d, non_blocking=True)
+        flat_d.copy_(flat_h, non_blocking=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(5):
+        flat_h.copy_(flat_d, non_blocking=True)
+    ev[1].record(stream)
+    for _ in range(5):
+        flat_d.copy_(flat_h, non_blocking=True)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    c_out = ev[0].elapsed_time(ev[1]) / 5
+    c_in = ev[1].elapsed_time(ev[2]) / 5
+    ms_out, ms_in = float(np.mean(t_out)), float(np.mean(t_in))
+    # the oracle's swap copy on the host, a bounded sample of the same pairs
+    k_np = np.zeros((npairs,) + tuple(cache.k_cache.shape[1:]), synth.STORAGE[wl.dtype])
+    v_np = np.zeros_like(k_np)
+    kh = np.empty_like(k_np)
+    vh = np.empty_like(v_np)
+    sample = [(i, i) for i in range(npairs)]
+    reps, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+        A.swap_blocks(k_np, v_np, kh, vh, sample)
+        reps += 1
+    cpu_s = (time.perf_counter() - t0) / reps
+    res = {
+        "metric": "swap of whole sequences to pinned host memory: GB/s of block bytes per "
+                  "direction",
+        "value": round(nbytes / (ms_out * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "higher_is_better": True, "data": "synthetic",
+        "dtype": wl.dtype,
+        "config": {"workload": wl.name, "swapped_seqs": len(out_set), "blocks": npairs,
+                   "bytes_each_way": nbytes},
+        "swap_out_ms": round(ms_out, 4), "swap_in_ms": round(ms_in, 4),
+        "swap_in_GBps": round(nbytes / (ms_in * 1e-3) / 1e9, 2),
+        "host_us_swap_out_call": round(float(np.median(host_out)), 1),
+        "host_us_swap_in_call": round(float(np.median(host_in)), 1),
+        "contiguous_copy_GBps": {"d2h": round(nbytes / (c_out * 1e-3) / 1e9, 2),
+                                 "h2d": round(nbytes / (c_in * 1e-3) / 1e9, 2)},
+        "roofline": {"bound": "host link", "achieved": round(nbytes / (ms_out * 1e-3) / 1e9, 2),
+                     "peak": HOST_LINK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (ms_out * 1e-3) / 1e9 / HOST_LINK_GBS, 4),
+                     "kernel": "swap_blocks_kernel (device -> pinned host)"},
+        "cpu_baseline": {"value": round(nbytes / cpu_s / 1e9, 2), "unit": "GB/s", "cores": 1,
+                         "kind": "oracle",
+                         "sample": f"oracle swap_blocks over the same {npairs} block pairs in "
+                                   f"host memory, repeated {reps}x"},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -214,6 +318,9 @@ def main():
         sys.exit(2)
     if args.calibrate:
         calibrate()
+        return
+    if args.swap:
+        bench_swap(args)
         return
     wl = synth.WORKLOADS[args.workload]
     part = wl.partition if args.partition is None else args.partition

@@ -126,6 +126,28 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
                          int dtype, void* stream);
 
 /*
+ * pa_swap_blocks — whole-block copies between two caches of the same
+ * geometry, for swapping sequences out to host memory and back (encyclopedia
+ * entry, "a ideia": the cache can be swapped to CPU RAM; "como funciona": a
+ * preempted sequence returns by swapping in).
+ *
+ *   src_k, src_v  cache to read, src_blocks blocks, layout above
+ *   dst_k, dst_v  cache to write, dst_blocks blocks, same layout
+ *   pairs  int32 [num_pairs][2] = {src, dst} block ids (from pa_seq_swap_out
+ *          or pa_seq_swap_in).  Pairs outside either cache are skipped; no
+ *          dst may repeat within a call.
+ * Each of the five arrays may be device memory or pinned host memory
+ * (hipHostMalloc); host memory is reached through its device mapping.
+ * Anything else (pageable host memory) is PA_ERR_INVALID.  num_pairs == 0 is
+ * a no-op.  Bit-exact.  Asynchronous on `stream`: a host cache holds the data
+ * once the stream has passed this call.
+ */
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, int src_blocks, void* dst_k,
+                         void* dst_v, int dst_blocks, const int32_t* pairs, int num_pairs,
+                         int num_kv_heads, int head_dim, int block_size, int dtype,
+                         void* stream);
+
+/*
  * Bytes of workspace pa_decode needs for these sizes; 0 when no sequence can
  * span more than one partition (partition_size == 0 or
  * max_context_len <= partition_size).
@@ -272,8 +294,51 @@ pa_status pa_seq_append(pa_pool* pool, int64_t seq, int num_tokens, int64_t* slo
 pa_status pa_seq_append_batch(pa_pool* pool, const int64_t* seqs, int n, int tokens_each,
                               int64_t* slots_out, int32_t* pairs_out, int* num_pairs_out);
 
-/* Release every block of seq in logical order and forget seq. */
+/* Release every block of seq in logical order (host blocks if it is swapped
+ * out) and forget seq. */
 pa_status pa_seq_free(pa_pool* pool, int64_t seq);
+
+/*
+ * Swapping whole sequences (encyclopedia entry, "como funciona": eviction
+ * takes all of a sequence's blocks or none; a preempted sequence returns by
+ * swap-in from CPU RAM or by recomputation, the latter being pa_seq_free plus
+ * a new prefill).
+ *
+ * pa_pool_set_host_blocks: give the pool num_host_blocks host block ids
+ * [0, num_host_blocks), free list FIFO in increasing order.  Resets the host
+ * area; PA_ERR_INVALID while any sequence is swapped out.
+ *
+ * pa_seq_swap_out: move seqs[0..n) (distinct, not swapped) to host blocks, all
+ * or nothing.  Each distinct GPU block that the batch's tables name, in order
+ * of first appearance (sequence order, then logical order), gets one host
+ * block (blocks shared inside the batch stay shared on the host).  Every table
+ * entry then names its host block and gives up its GPU reference, released in
+ * the same order.  pairs_out [cap][2] receives {gpu block, host block} per
+ * distinct block and *num_pairs_out their count: run pa_swap_blocks(device ->
+ * host) with them before anything else writes the released GPU blocks.
+ * PA_ERR_NO_BLOCKS (nothing changes) if the host free list is too short;
+ * PA_ERR_INVALID if cap is too small, a sequence is already swapped or ids
+ * repeat; PA_ERR_UNKNOWN_SEQ for an unknown id (checked first).
+ *
+ * pa_seq_swap_in: the mirror image for swapped seqs: each distinct host block
+ * gets a new GPU block (FIFO; refcount = references from the batch), host
+ * references are released in order, pairs_out receives {host block, GPU
+ * block}: run pa_swap_blocks(host -> device) before decoding them.
+ * PA_ERR_NO_BLOCKS (nothing changes) if the GPU free list is too short.
+ *
+ * A swapped sequence cannot be appended to, forked or put in
+ * pa_pool_block_tables (PA_ERR_INVALID); pa_seq_block_table returns its host
+ * block ids; pa_seq_free releases them.
+ */
+pa_status pa_pool_set_host_blocks(pa_pool* pool, int num_host_blocks);
+pa_status pa_seq_swap_out(pa_pool* pool, const int64_t* seqs, int n, int32_t* pairs_out,
+                          int cap, int* num_pairs_out);
+pa_status pa_seq_swap_in(pa_pool* pool, const int64_t* seqs, int n, int32_t* pairs_out,
+                         int cap, int* num_pairs_out);
+/* 1 if seq is swapped out, 0 if on the GPU, -1 if unknown. */
+int pa_seq_is_swapped(const pa_pool* pool, int64_t seq);
+/* stats_out[3] = {free host blocks, host blocks in use, swapped sequences}. */
+pa_status pa_pool_host_stats(const pa_pool* pool, int64_t* stats_out);
 
 /* Copy seq's block table into out[0..cap); *num_blocks_out, *num_tokens_out get
  * its length and fill.  PA_ERR_INVALID if cap is too small (nothing copied). */

@@ -210,6 +210,15 @@ def write_kv(k_cache, v_cache, k_new, v_new, slots):
     v_cache[b, :, t // x, :, t % x] = vn
 
 
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs):
+    """Swap copies between a GPU cache and a host cache (tonho.wtf, "a ideia":
+    swap to CPU RAM): for each (src, dst) pair the whole block of K and of V
+    moves from the source cache to the destination cache."""
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        dst_k[dst] = src_k[src]
+        dst_v[dst] = src_v[src]
+
+
 def copy_blocks(k_cache, v_cache, pairs):
     """For each (src, dst) pair in order, copy the whole physical block (all
     heads, all positions) of K and of V."""

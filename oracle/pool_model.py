@@ -26,6 +26,23 @@ bit (the C++ pool implements the same policy):
   * append is all-or-nothing: if the free list cannot cover the call, nothing
     changes and NO_BLOCKS is returned; a batch append is all-or-nothing over the
     whole batch, processed in the order given.
+
+Swapping (tonho.wtf, "a ideia": the cache can be swapped out to CPU RAM;
+"como funciona": eviction takes all of a sequence's blocks or none, and a
+preempted sequence comes back by swapping in or by recomputing).  Readings:
+  * host blocks are a second pool of ids [0, H) with its own FIFO free list
+    (initial order 0..H-1) and reference counts;
+  * swap_out(seqs) moves the whole batch or nothing: every distinct GPU block
+    the batch's tables name (first appearance: sequence order, then logical
+    order) gets one host block, so blocks shared inside the batch stay shared
+    on the host; each table entry then names the host block and gives up its
+    GPU reference (released in the same order); the pairs (gpu, host) are the
+    copies the device must make before a released GPU block is reused;
+  * swap_in(seqs) is the mirror image: distinct host blocks get new GPU blocks
+    in first-appearance order, refcount = references from the batch, host
+    references released in order; pairs (host, gpu);
+  * a swapped sequence cannot be appended to, forked or decoded; freeing it
+    (the recompute choice) releases its host blocks.
 """
 from __future__ import annotations
 
@@ -48,6 +65,16 @@ class PoolModel:
         self.tables: dict[int, list[int]] = {}
         self.fill: dict[int, int] = {}
         self.copies = 0
+        self.swapped: set[int] = set()
+        self.host_free = deque()
+        self.host_ref: list[int] = []
+
+    def set_host_blocks(self, n: int) -> int:
+        if n < 0 or self.swapped:
+            return INVALID
+        self.host_free = deque(range(n))
+        self.host_ref = [0] * n
+        return OK
 
     # -- block primitives ----------------------------------------------------
     def _alloc(self) -> int:
@@ -71,7 +98,7 @@ class PoolModel:
     def fork(self, parent: int, child: int) -> int:
         if parent not in self.tables:
             return UNKNOWN_SEQ
-        if child in self.tables:
+        if child in self.tables or parent in self.swapped:
             return INVALID
         self.tables[child] = list(self.tables[parent])
         self.fill[child] = self.fill[parent]
@@ -82,10 +109,85 @@ class PoolModel:
     def free_seq(self, sid: int) -> int:
         if sid not in self.tables:
             return UNKNOWN_SEQ
-        for b in self.tables.pop(sid):
-            self._release(b)
+        if sid in self.swapped:
+            self.swapped.discard(sid)
+            for h in self.tables.pop(sid):
+                self._host_release(h)
+        else:
+            for b in self.tables.pop(sid):
+                self._release(b)
         del self.fill[sid]
         return OK
+
+    def _host_release(self, h: int):
+        self.host_ref[h] -= 1
+        if self.host_ref[h] == 0:
+            self.host_free.append(h)
+
+    def _batch_ok(self, sids, want_swapped: bool) -> int:
+        for s in sids:
+            if s not in self.tables:
+                return UNKNOWN_SEQ
+        for s in sids:
+            if (s in self.swapped) != want_swapped:
+                return INVALID
+        if len(set(sids)) != len(sids):
+            return INVALID
+        return OK
+
+    def _distinct(self, sids):
+        seen = {}
+        for s in sids:
+            for b in self.tables[s]:
+                if b not in seen:
+                    seen[b] = len(seen)
+        return list(seen)
+
+    def swap_out(self, sids):
+        """Returns (status, pairs [(gpu, host), ...])."""
+        st = self._batch_ok(sids, False)
+        if st != OK:
+            return st, []
+        blocks = self._distinct(sids)
+        if len(blocks) > len(self.host_free):
+            return NO_BLOCKS, []
+        to_host = {b: self.host_free.popleft() for b in blocks}
+        for s in sids:
+            new = []
+            for b in self.tables[s]:
+                self.host_ref[to_host[b]] += 1
+                self._release(b)
+                new.append(to_host[b])
+            self.tables[s] = new
+            self.swapped.add(s)
+        return OK, [(b, to_host[b]) for b in blocks]
+
+    def swap_in(self, sids):
+        """Returns (status, pairs [(host, gpu), ...])."""
+        st = self._batch_ok(sids, True)
+        if st != OK:
+            return st, []
+        hosts = self._distinct(sids)
+        if len(hosts) > len(self.free):
+            return NO_BLOCKS, []
+        to_gpu = {}
+        for h in hosts:
+            to_gpu[h] = self.free.popleft()
+            self.ref[to_gpu[h]] = 0
+        for s in sids:
+            new = []
+            for h in self.tables[s]:
+                self.ref[to_gpu[h]] += 1
+                self._host_release(h)
+                new.append(to_gpu[h])
+            self.tables[s] = new
+            self.swapped.discard(s)
+        return OK, [(h, to_gpu[h]) for h in hosts]
+
+    def host_stats(self):
+        return {"host_free": len(self.host_free),
+                "host_used": sum(1 for r in self.host_ref if r > 0),
+                "swapped": len(self.swapped)}
 
     def _needed(self, sid: int, k: int, ref) -> int:
         """Blocks that append(sid, k) takes, given refcounts `ref`."""
@@ -122,11 +224,11 @@ class PoolModel:
         (status, slots [len(sids)*k], pairs [(src, dst), ...])."""
         if k < 0:
             return INVALID, [], []
-        if len(set(sids)) != len(sids):
-            return INVALID, [], []
         for s in sids:
             if s not in self.tables:
                 return UNKNOWN_SEQ, [], []
+        if any(s in self.swapped for s in sids) or len(set(sids)) != len(sids):
+            return INVALID, [], []
         # dry run of the refcount changes to count the blocks the batch takes
         ref = {}
         need = 0

@@ -38,6 +38,12 @@ SIGNATURES = {
     "pa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                        _i, _vp, _sz, _i, _i, _vp]),
     "pa_decode_order": (_i, [_vp, _i, _vp, _i, _vp]),
+    "pa_swap_blocks": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _vp]),
+    "pa_pool_set_host_blocks": (_i, [_vp, _i]),
+    "pa_seq_swap_out": (_i, [_vp, _vp, _i, _vp, _i, _vp]),
+    "pa_seq_swap_in": (_i, [_vp, _vp, _i, _vp, _i, _vp]),
+    "pa_seq_is_swapped": (_i, [_vp, _i64]),
+    "pa_pool_host_stats": (_i, [_vp, _vp]),
     "pa_decode_step_staging_size": (_sz, [_i, _i]),
     "pa_decode_step": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _f,
                             _i, _i, _vp, _vp, _sz, _vp, _sz, _i, _vp]),
@@ -118,6 +124,15 @@ def _dev_ptr(t, name: str) -> int:
     return t.data_ptr()
 
 
+def _any_ptr(t, name: str) -> int:
+    """GPU tensor or pinned CPU tensor (device-reachable memory)."""
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
+    return t.data_ptr()
+
+
 def _stream_ptr(stream) -> int:
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -172,6 +187,26 @@ def pa_copy_blocks(k_cache, v_cache, pairs, stream=None):
                               _dev_ptr(pairs, "pairs"), P, nb, H, d, bs,
                               torch_dtype_code(k_cache), _stream_ptr(stream))
     _check(st, "pa_copy_blocks")
+
+
+def pa_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None):
+    """Whole-block copies src -> dst between two caches of one geometry (GPU
+    tensors or pinned CPU tensors); pairs int32 [P][2] (GPU or pinned)."""
+    torch = _torch()
+    nb_s, H, bs, d = cache_geometry(src_k, src_v)
+    nb_d, H2, bs2, d2 = cache_geometry(dst_k, dst_v)
+    if (H, bs, d) != (H2, bs2, d2) or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination caches differ in geometry or dtype")
+    if pairs.dtype != torch.int32:
+        raise TypeError("pairs must be int32")
+    P = pairs.numel() // 2
+    if P == 0:
+        return
+    st = lib().pa_swap_blocks(_any_ptr(src_k, "src_k"), _any_ptr(src_v, "src_v"), nb_s,
+                              _any_ptr(dst_k, "dst_k"), _any_ptr(dst_v, "dst_v"), nb_d,
+                              _any_ptr(pairs, "pairs"), P, H, d, bs, torch_dtype_code(src_k),
+                              _stream_ptr(stream))
+    _check(st, "pa_swap_blocks")
 
 
 def pa_decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int,
@@ -352,3 +387,40 @@ class Pool:
         s = np.zeros(5, dtype=np.int64)
         _check(lib().pa_pool_stats(self._h, _np_ptr(s)), "pa_pool_stats")
         return dict(zip(("free", "used", "shared", "tokens", "copies"), s.tolist()))
+
+    # -- swapping ----------------------------------------------------------------
+    def set_host_blocks(self, n: int) -> int:
+        st = lib().pa_pool_set_host_blocks(self._h, n)
+        if st == PA_OK:
+            self.num_host_blocks = n
+        return st
+
+    def _swap(self, fn, seqs, cap=None):
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        if cap is None:
+            cap = 0
+            for s in seqs.tolist():
+                nb, nt = ctypes.c_int(0), ctypes.c_int(0)
+                st = lib().pa_seq_block_table(self._h, s, None, 0, ctypes.byref(nb),
+                                              ctypes.byref(nt))
+                cap += nb.value if st in (PA_OK, PA_ERR_INVALID) else 0
+        pairs = np.empty((max(1, cap), 2), dtype=np.int32)
+        n = ctypes.c_int(0)
+        st = fn(self._h, _np_ptr(seqs), seqs.size, _np_ptr(pairs), cap, ctypes.byref(n))
+        return st, (pairs[:n.value] if st == PA_OK else pairs[:0])
+
+    def swap_out(self, seqs, cap=None):
+        """-> (status, pairs int32 [n][2] = {gpu block, host block})."""
+        return self._swap(lib().pa_seq_swap_out, seqs, cap)
+
+    def swap_in(self, seqs, cap=None):
+        """-> (status, pairs int32 [n][2] = {host block, gpu block})."""
+        return self._swap(lib().pa_seq_swap_in, seqs, cap)
+
+    def is_swapped(self, seq: int) -> int:
+        return lib().pa_seq_is_swapped(self._h, seq)
+
+    def host_stats(self):
+        s = np.zeros(3, dtype=np.int64)
+        _check(lib().pa_pool_host_stats(self._h, _np_ptr(s)), "pa_pool_host_stats")
+        return dict(zip(("host_free", "host_used", "swapped"), s.tolist()))

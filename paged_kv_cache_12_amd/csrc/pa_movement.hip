@@ -67,6 +67,44 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ kc
     to[i] = from[i];
 }
 
+// Whole-block copies between two caches of the same geometry (device memory
+// or pinned host memory reached through its device mapping): grid (chunks,
+// pairs, 2), z = 0 for K, 1 for V.  Pairs outside either cache are skipped.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    const u32x4* __restrict__ src_k, const u32x4* __restrict__ src_v, u32x4* __restrict__ dst_k,
+    u32x4* __restrict__ dst_v, const int32_t* __restrict__ pairs, int src_blocks, int dst_blocks,
+    int64_t vecs_per_block) {
+  const int pi = blockIdx.y;
+  const int32_t src = pairs[2 * pi];
+  const int32_t dst = pairs[2 * pi + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const u32x4* from = (blockIdx.z ? src_v : src_k) + src * vecs_per_block;
+  u32x4* to = (blockIdx.z ? dst_v : dst_k) + dst * vecs_per_block;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < vecs_per_block;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    to[i] = from[i];
+}
+
+// Device-side address of a cache or pair array: device memory as is, pinned
+// host memory through its device mapping; nullptr for anything else.
+void* device_view(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (a.type == hipMemoryTypeDevice) return const_cast<void*>(p);
+  if (a.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    return d;
+  }
+  return nullptr;
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -127,5 +165,39 @@ PA_EXPORT pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* 
                      dim3(threads), 0, static_cast<hipStream_t>(stream),
                      static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), pairs,
                      num_blocks, vecs);
+  return launch_status();
+}
+
+PA_EXPORT pa_status pa_swap_blocks(const void* src_k, const void* src_v, int src_blocks,
+                                   void* dst_k, void* dst_v, int dst_blocks,
+                                   const int32_t* pairs, int num_pairs, int num_kv_heads,
+                                   int head_dim, int block_size, int dtype, void* stream) {
+  const int e = elem_bytes(dtype);
+  if (e == 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs < 0 || src_blocks <= 0 || dst_blocks <= 0 || num_kv_heads <= 0)
+    return PA_ERR_INVALID;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !pairs) return PA_ERR_INVALID;
+  if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v))
+    return PA_ERR_INVALID;
+  if (num_pairs > 65535) return PA_ERR_INVALID;
+  const void* sk = device_view(src_k);
+  const void* sv = device_view(src_v);
+  void* dk = device_view(dst_k);
+  void* dv = device_view(dst_v);
+  const void* pp = device_view(pairs);
+  if (!sk || !sv || !dk || !dv || !pp) return PA_ERR_INVALID;
+  const int64_t vecs = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * e / 16;
+  const int threads = 256;
+  int64_t chunks = (vecs + threads * 4 - 1) / (threads * 4);
+  if (chunks < 1) chunks = 1;
+  if (chunks > 1024) chunks = 1024;
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(static_cast<unsigned>(chunks), num_pairs, 2),
+                     dim3(threads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(sk), static_cast<const u32x4*>(sv),
+                     static_cast<u32x4*>(dk), static_cast<u32x4*>(dv),
+                     static_cast<const int32_t*>(pp), src_blocks, dst_blocks, vecs);
   return launch_status();
 }

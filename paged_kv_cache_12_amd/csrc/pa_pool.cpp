@@ -1,8 +1,10 @@
 // Host-side KV block pool: per-sequence block tables, refcounts, fork / append /
 // free and copy-on-write decisions (vLLM encyclopedia entry, tonho.wtf, section
-// "como funciona").  Host memory only; no HIP calls.
+// "como funciona"), and swapping whole sequences to host blocks and back
+// (same entry, "a ideia" and "como funciona": swap to CPU RAM, eviction all or
+// nothing per sequence).  Host memory only; no HIP calls.
 //
-// The free list is a ring buffer holding each free block id once (FIFO: take
+// Each free list is a ring buffer holding each free block id once (FIFO: take
 // from the front, return to the back).  Sequences live in a hash map keyed by
 // the caller's 64-bit id.  Every operation is O(tokens + blocks touched).
 #include <algorithm>
@@ -19,8 +21,31 @@
 namespace {
 
 struct Seq {
-  std::vector<int32_t> table;
+  std::vector<int32_t> table;  // GPU block ids, or host block ids when swapped
   int64_t fill = 0;
+  bool swapped = false;
+};
+
+// FIFO of free block ids over [0, n)
+struct Ring {
+  std::vector<int32_t> buf;
+  int64_t head = 0, count = 0;
+  void init(int32_t n, const int32_t* order) {
+    buf.resize(n);
+    for (int32_t i = 0; i < n; ++i) buf[i] = order ? order[i] : i;
+    head = 0;
+    count = n;
+  }
+  int32_t pop() {
+    const int32_t b = buf[head];
+    head = (head + 1) % static_cast<int64_t>(buf.size());
+    --count;
+    return b;
+  }
+  void push(int32_t b) {
+    buf[(head + count) % static_cast<int64_t>(buf.size())] = b;
+    ++count;
+  }
 };
 
 }  // namespace
@@ -36,6 +61,11 @@ struct pa_pool {
   int64_t copies = 0;
   int64_t tokens = 0;
   int64_t shared = 0;  // blocks with refcount > 1
+  // host blocks for swapped sequences
+  Ring host;
+  std::vector<int32_t> host_ref;
+  int64_t host_used = 0;
+  int64_t swapped = 0;  // swapped sequences
 
   int32_t alloc() {
     int32_t b = ring[head];
@@ -52,6 +82,12 @@ struct pa_pool {
     if (--ref[b] == 0) {
       ring[(head + count) % num_blocks] = b;
       ++count;
+    }
+  }
+  void host_release(int32_t h) {
+    if (--host_ref[h] == 0) {
+      host.push(h);
+      --host_used;
     }
   }
 };
@@ -136,7 +172,7 @@ PA_EXPORT pa_status pa_seq_fork(pa_pool* p, int64_t parent, int64_t child) {
   if (!p) return PA_ERR_INVALID;
   auto it = p->seqs.find(parent);
   if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
-  if (p->seqs.count(child)) return PA_ERR_INVALID;
+  if (p->seqs.count(child) || it->second.swapped) return PA_ERR_INVALID;
   Seq c = it->second;  // copy before emplace (rehash may move it)
   for (int32_t b : c.table) p->retain(b);
   p->tokens += c.fill;
@@ -158,6 +194,8 @@ PA_EXPORT pa_status pa_seq_append_batch(pa_pool* p, const int64_t* seqs, int n, 
     if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
     ss[i] = &it->second;
   }
+  for (int i = 0; i < n; ++i)
+    if (ss[i]->swapped) return PA_ERR_INVALID;
   {
     std::vector<int64_t> ids(seqs, seqs + n);
     std::sort(ids.begin(), ids.end());
@@ -201,7 +239,12 @@ PA_EXPORT pa_status pa_seq_free(pa_pool* p, int64_t seq) {
   if (!p) return PA_ERR_INVALID;
   auto it = p->seqs.find(seq);
   if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
-  for (int32_t b : it->second.table) p->release(b);
+  if (it->second.swapped) {
+    for (int32_t h : it->second.table) p->host_release(h);
+    --p->swapped;
+  } else {
+    for (int32_t b : it->second.table) p->release(b);
+  }
   p->tokens -= it->second.fill;
   p->seqs.erase(it);
   return PA_OK;
@@ -230,6 +273,7 @@ PA_EXPORT pa_status pa_pool_block_tables(const pa_pool* p, const int64_t* seqs, 
   for (int i = 0; i < n; ++i) {
     auto it = p->seqs.find(seqs[i]);
     if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+    if (it->second.swapped) return PA_ERR_INVALID;
     if (static_cast<int64_t>(it->second.table.size()) > maxb) return PA_ERR_INVALID;
     ss[i] = &it->second;
   }
@@ -273,6 +317,134 @@ PA_EXPORT pa_status pa_pool_stats(const pa_pool* p, int64_t* stats_out) {
 // sequence, O(1).
 extern "C" __attribute__((visibility("hidden"))) int64_t pa_pool_shared_blocks(const pa_pool* p) {
   return p ? p->shared : 0;
+}
+
+PA_EXPORT pa_status pa_pool_set_host_blocks(pa_pool* p, int num_host_blocks) {
+  if (!p || num_host_blocks < 0) return PA_ERR_INVALID;
+  if (p->swapped > 0) return PA_ERR_INVALID;
+  p->host.init(num_host_blocks, nullptr);
+  p->host_ref.assign(num_host_blocks, 0);
+  p->host_used = 0;
+  return PA_OK;
+}
+
+namespace {
+
+// Resolve a batch of distinct ids whose swapped state is `want_swapped`.
+pa_status resolve_batch(pa_pool* p, const int64_t* seqs, int n, bool want_swapped,
+                        std::vector<Seq*>& out) {
+  if (n < 0 || (n > 0 && !seqs)) return PA_ERR_INVALID;
+  out.resize(n);
+  for (int i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+    out[i] = &it->second;
+  }
+  for (int i = 0; i < n; ++i)
+    if (out[i]->swapped != want_swapped) return PA_ERR_INVALID;
+  std::vector<int64_t> ids(seqs, seqs + n);
+  std::sort(ids.begin(), ids.end());
+  if (std::adjacent_find(ids.begin(), ids.end()) != ids.end()) return PA_ERR_INVALID;
+  return PA_OK;
+}
+
+// Distinct block ids of the batch's tables in order of first appearance
+// (sequence order, then logical order); `slot` maps an id to its index.
+void distinct_blocks(const std::vector<Seq*>& ss, std::vector<int32_t>& uniq,
+                     std::unordered_map<int32_t, int32_t>& slot) {
+  for (const Seq* s : ss)
+    for (int32_t b : s->table)
+      if (slot.emplace(b, static_cast<int32_t>(uniq.size())).second) uniq.push_back(b);
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_seq_swap_out(pa_pool* p, const int64_t* seqs, int n, int32_t* pairs_out,
+                                    int cap, int* num_pairs_out) {
+  if (!p || cap < 0) return PA_ERR_INVALID;
+  if (num_pairs_out) *num_pairs_out = 0;
+  std::vector<Seq*> ss;
+  pa_status st = resolve_batch(p, seqs, n, false, ss);
+  if (st != PA_OK) return st;
+  std::vector<int32_t> uniq;
+  std::unordered_map<int32_t, int32_t> slot;
+  distinct_blocks(ss, uniq, slot);
+  const int64_t k = static_cast<int64_t>(uniq.size());
+  if (k > cap || (k > 0 && !pairs_out)) return PA_ERR_INVALID;
+  if (k > p->host.count) return PA_ERR_NO_BLOCKS;
+  std::vector<int32_t> hb(k);
+  for (int64_t i = 0; i < k; ++i) {
+    hb[i] = p->host.pop();
+    pairs_out[2 * i] = uniq[i];
+    pairs_out[2 * i + 1] = hb[i];
+  }
+  p->host_used += k;
+  for (Seq* s : ss) {
+    for (int32_t& b : s->table) {
+      const int32_t h = hb[slot[b]];
+      ++p->host_ref[h];
+      p->release(b);
+      b = h;
+    }
+    s->swapped = true;
+    ++p->swapped;
+  }
+  if (num_pairs_out) *num_pairs_out = static_cast<int>(k);
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_seq_swap_in(pa_pool* p, const int64_t* seqs, int n, int32_t* pairs_out,
+                                   int cap, int* num_pairs_out) {
+  if (!p || cap < 0) return PA_ERR_INVALID;
+  if (num_pairs_out) *num_pairs_out = 0;
+  std::vector<Seq*> ss;
+  pa_status st = resolve_batch(p, seqs, n, true, ss);
+  if (st != PA_OK) return st;
+  std::vector<int32_t> uniq;
+  std::unordered_map<int32_t, int32_t> slot;
+  distinct_blocks(ss, uniq, slot);
+  const int64_t k = static_cast<int64_t>(uniq.size());
+  if (k > cap || (k > 0 && !pairs_out)) return PA_ERR_INVALID;
+  if (k > p->count) return PA_ERR_NO_BLOCKS;
+  std::vector<int32_t> gb(k);
+  std::vector<char> first(k, 1);
+  for (int64_t i = 0; i < k; ++i) {
+    gb[i] = p->alloc();
+    pairs_out[2 * i] = uniq[i];
+    pairs_out[2 * i + 1] = gb[i];
+  }
+  for (Seq* s : ss) {
+    for (int32_t& h : s->table) {
+      const int32_t j = slot[h];
+      const int32_t g = gb[j];
+      if (first[j]) {
+        first[j] = 0;  // alloc() gave the first reference
+      } else {
+        p->retain(g);
+      }
+      p->host_release(h);
+      h = g;
+    }
+    s->swapped = false;
+    --p->swapped;
+  }
+  if (num_pairs_out) *num_pairs_out = static_cast<int>(k);
+  return PA_OK;
+}
+
+PA_EXPORT int pa_seq_is_swapped(const pa_pool* p, int64_t seq) {
+  if (!p) return -1;
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return -1;
+  return it->second.swapped ? 1 : 0;
+}
+
+PA_EXPORT pa_status pa_pool_host_stats(const pa_pool* p, int64_t* stats_out) {
+  if (!p || !stats_out) return PA_ERR_INVALID;
+  stats_out[0] = p->host.count;
+  stats_out[1] = p->host_used;
+  stats_out[2] = p->swapped;
+  return PA_OK;
 }
 
 PA_EXPORT pa_status pa_decode_order(const int32_t* block_tables, int max_blocks_per_seq,

@@ -6,13 +6,15 @@ with each iteration's input.  PagedKVCache is that manager for one GPU: the C++
 pool decides slots and copy-on-write pairs, and the device operations
 (pa_copy_blocks, pa_write_kv, pa_decode) run on the caller's stream.  Metadata
 goes to the device through pinned host buffers with asynchronous copies.
+Whole sequences can be swapped out to pinned host blocks and back (same
+entry, "a ideia" and "como funciona").
 """
 from __future__ import annotations
 
 import numpy as np
 
 from . import (Pool, PA_OK, PA_DECODE_SHARED_KV, PAError, pa_copy_blocks, pa_decode,
-               pa_decode_order, pa_decode_workspace_size, pa_write_kv)
+               pa_decode_order, pa_decode_workspace_size, pa_swap_blocks, pa_write_kv)
 
 TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
 
@@ -84,6 +86,47 @@ class PagedKVCache:
         st = self.pool.free(seq)
         if st != PA_OK:
             raise PAError(st, "pa_seq_free")
+
+    # -- swapping to pinned host memory -----------------------------------------
+    def enable_swap(self, num_host_blocks: int):
+        """Pinned host caches of num_host_blocks blocks (same layout) and the
+        pool's host block ids."""
+        torch = self.torch
+        kshape = (num_host_blocks,) + tuple(self.k_cache.shape[1:])
+        vshape = (num_host_blocks,) + tuple(self.v_cache.shape[1:])
+        self.k_host = torch.empty(kshape, dtype=self.tdtype, pin_memory=True)
+        self.v_host = torch.empty(vshape, dtype=self.tdtype, pin_memory=True)
+        st = self.pool.set_host_blocks(num_host_blocks)
+        if st != PA_OK:
+            raise PAError(st, "pa_pool_set_host_blocks")
+
+    def _pairs_to_device(self, pairs):
+        # through pinned memory, so the host does not wait for earlier work on
+        # the stream
+        t = self.torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).pin_memory()
+        return t.to(self.device, non_blocking=True)
+
+    def swap_out(self, seqs, stream=None):
+        """Move seqs (all or none) to host blocks; the device -> host copies run
+        on `stream`.  Returns the (gpu, host) pairs."""
+        st, pairs = self.pool.swap_out(np.asarray(seqs, dtype=np.int64))
+        if st != PA_OK:
+            raise PAError(st, "pa_seq_swap_out")
+        if len(pairs):
+            pa_swap_blocks(self.k_cache, self.v_cache, self.k_host, self.v_host,
+                           self._pairs_to_device(pairs), stream=stream)
+        return pairs
+
+    def swap_in(self, seqs, stream=None):
+        """Bring swapped seqs back (all or none); host -> device copies on
+        `stream`.  Returns the (host, gpu) pairs."""
+        st, pairs = self.pool.swap_in(np.asarray(seqs, dtype=np.int64))
+        if st != PA_OK:
+            raise PAError(st, "pa_seq_swap_in")
+        if len(pairs):
+            pa_swap_blocks(self.k_host, self.v_host, self.k_cache, self.v_cache,
+                           self._pairs_to_device(pairs), stream=stream)
+        return pairs
 
     # -- append: pool slots, copy-on-write, block write ----------------------
     def append(self, seqs, k: int, k_new, v_new, stream=None):

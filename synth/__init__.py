@@ -231,7 +231,7 @@ def build_scenario(wl: Workload, batch: int | None = None, ctx_hi: int | None = 
         lengths["gen"] = gens
         need = int(sum(_ceil_div(int(n), bs) for n in plen))
         need += int(sum(_ceil_div(int(x), bs) + 1 for x in gens))
-        nblocks = int(math.ceil(1.25 * need))
+        nblocks = wl.pool_blocks or int(math.ceil(1.25 * need))
         free_order = g.permutation(nblocks).astype(np.int32)
         key = 0
         for p in range(P):
@@ -249,7 +249,7 @@ def build_scenario(wl: Workload, batch: int | None = None, ctx_hi: int | None = 
         sfx = g.integers(wl.ctx_lo, hi, size=B, endpoint=True)
         lengths["suffix"] = sfx
         need = _ceil_div(wl.prefix_len, bs) + int(sum(_ceil_div(int(x), bs) + 1 for x in sfx))
-        nblocks = int(math.ceil(1.25 * need))
+        nblocks = wl.pool_blocks or int(math.ceil(1.25 * need))
         free_order = g.permutation(nblocks).astype(np.int32)
         tmpl = B  # template sequence id, freed after the forks
         ops.append(("create", tmpl))

@@ -54,6 +54,26 @@ class OracleSide:
     def write(self, slots, kv, vv):
         self.A.write_kv(self.kc, self.vc, kv, vv, slots)
 
+    def enable_swap(self, n):
+        assert self.pool.set_host_blocks(n) == 0
+        self.kh = np.empty((n,) + self.kc.shape[1:], dtype=self.kc.dtype)
+        self.vh = np.empty((n,) + self.vc.shape[1:], dtype=self.vc.dtype)
+        ib = np.uint32 if self.wl.dtype == "f32" else np.uint16
+        self.kh.view(ib)[...] = synth.poison_bits(self.wl.dtype)
+        self.vh.view(ib)[...] = synth.poison_bits(self.wl.dtype)
+
+    def swap_out(self, seqs):
+        st, pairs = self.pool.swap_out(list(seqs))
+        assert st == 0, st
+        self.A.swap_blocks(self.kc, self.vc, self.kh, self.vh, pairs)
+        return np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
+
+    def swap_in(self, seqs):
+        st, pairs = self.pool.swap_in(list(seqs))
+        assert st == 0, st
+        self.A.swap_blocks(self.kh, self.vh, self.kc, self.vc, pairs)
+        return np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
+
     def tables(self, seqs):
         ts = [self.pool.block_table(s) for s in seqs]
         maxb = max(1, max(len(t) for t, _ in ts))
@@ -110,6 +130,21 @@ class GpuSide:
         kd = storage_to_torch(kv, self.wl.dtype).cuda()
         vd = storage_to_torch(vv, self.wl.dtype).cuda()
         pa_write_kv(kd, vd, self.cache.k_cache, self.cache.v_cache, ds, stream=self.stream)
+
+    def enable_swap(self, n):
+        self.cache.enable_swap(n)
+        t = self.torch
+        ib = t.int32 if self.wl.dtype == "f32" else t.int16
+        bits = synth.poison_bits(self.wl.dtype)
+        val = bits if bits < (1 << (8 * ib.itemsize - 1)) else bits - (1 << (8 * ib.itemsize))
+        self.cache.k_host.view(ib).fill_(val)
+        self.cache.v_host.view(ib).fill_(val)
+
+    def swap_out(self, seqs):
+        return self.cache.swap_out(seqs, stream=self.stream)
+
+    def swap_in(self, seqs):
+        return self.cache.swap_in(seqs, stream=self.stream)
 
     def tables(self, seqs):
         return self.cache.tables(seqs)

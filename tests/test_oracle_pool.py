@@ -13,8 +13,13 @@ GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def check_invariants(p: PoolModel):
-    # every reference is a table entry and vice versa
-    assert sum(p.ref) == sum(len(t) for t in p.tables.values())
+    # every reference is a table entry and vice versa (host blocks for
+    # swapped sequences)
+    assert sum(p.ref) == sum(len(t) for s, t in p.tables.items() if s not in p.swapped)
+    assert sum(p.host_ref) == sum(len(t) for s, t in p.tables.items() if s in p.swapped)
+    assert len(set(p.host_free)) == len(p.host_free)
+    assert all(p.host_ref[h] == 0 for h in p.host_free)
+    assert sum(1 for r in p.host_ref if r > 0) + len(p.host_free) == len(p.host_ref)
     # free list: distinct, unreferenced; free + used = all blocks
     assert len(set(p.free)) == len(p.free)
     assert all(p.ref[b] == 0 for b in p.free)
@@ -216,3 +221,146 @@ def test_kv_size_factors():
     assert kv_bytes_per_token(3, 5, 7, 2) == 2 * 3 * 5 * 7 * 2
     # the Llama-3-8B-class page figure: 100,000 tokens are 12.8 million KiB
     assert kv_bytes(100000, 32, 8, 128, 2) == 12_800_000 * 1024
+
+
+# -- swapping (tonho.wtf "a ideia", "como funciona") ---------------------------
+
+class ContentModel:
+    """Token payloads per physical slot, moved by the pairs the pool returns
+    exactly as the device would move K/V: a sequence must always read back the
+    tokens written for it, in order."""
+
+    def __init__(self, p: PoolModel):
+        self.p = p
+        self.gpu = {}    # block -> list of bs payloads
+        self.host = {}
+        self.expect = {}
+
+    def new(self, sid):
+        assert self.p.create(sid) == OK
+        self.expect[sid] = []
+
+    def fork(self, parent, child):
+        if self.p.fork(parent, child) == OK:
+            self.expect[child] = list(self.expect[parent])
+
+    def append(self, sids, k, rng):
+        st, slots, pairs = self.p.append_batch(sids, k)
+        if st != OK:
+            return
+        for src, dst in pairs:
+            self.gpu[dst] = list(self.gpu[src])
+        i = 0
+        for s in sids:
+            for _ in range(k):
+                tok = rng.randrange(1 << 30)
+                b, o = divmod(slots[i], self.p.bs)
+                self.gpu.setdefault(b, [None] * self.p.bs)[o] = tok
+                self.expect[s].append(tok)
+                i += 1
+
+    def swap_out(self, sids):
+        st, pairs = self.p.swap_out(sids)
+        for g, h in pairs:
+            self.host[h] = list(self.gpu[g])
+        return st
+
+    def swap_in(self, sids):
+        st, pairs = self.p.swap_in(sids)
+        for h, g in pairs:
+            self.gpu[g] = list(self.host[h])
+        return st
+
+    def free(self, sid):
+        assert self.p.free_seq(sid) == OK
+        del self.expect[sid]
+
+    def check(self):
+        for s, want in self.expect.items():
+            table, n = self.p.block_table(s)
+            src = self.host if s in self.p.swapped else self.gpu
+            got = [src[table[t // self.p.bs]][t % self.p.bs] for t in range(n)]
+            assert got == want, s
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_swap_round_trip_keeps_every_sequence_content(seed):
+    rng = random.Random(seed)
+    p = PoolModel(96, 8, rng.sample(range(96), 96))
+    p.set_host_blocks(64)
+    c = ContentModel(p)
+    live, nxt = [], 0
+    for it in range(1500):
+        r = rng.random()
+        if r < 0.08 or not live:
+            c.new(nxt); live.append(nxt); nxt += 1
+        elif r < 0.15:
+            c.fork(rng.choice(live), nxt)
+            if nxt in p.tables:
+                live.append(nxt)
+            nxt += 1
+        elif r < 0.2:
+            s = rng.choice(live); live.remove(s); c.free(s)
+        elif r < 0.3:
+            c.swap_out(rng.sample(live, min(len(live), rng.randint(1, 4))))
+        elif r < 0.4:
+            off = [s for s in live if s in p.swapped]
+            if off:
+                c.swap_in(rng.sample(off, min(len(off), rng.randint(1, 4))))
+        else:
+            on = [s for s in live if s not in p.swapped]
+            if on:
+                c.append(rng.sample(on, min(len(on), rng.randint(1, 4))),
+                         rng.choice([1, 1, 3, 8, 17]), rng)
+        check_invariants(p)
+        c.check()
+
+
+def test_swap_keeps_sharing_inside_a_batch_and_frees_gpu_blocks():
+    p = PoolModel(12, 4)
+    p.set_host_blocks(12)
+    p.create(0)
+    p.append(0, 10)                      # 3 blocks, last one half full
+    for child in (1, 2, 3):
+        p.fork(0, child)                 # refcount 4 on all three
+    free_before = len(p.free)
+    st, pairs = p.swap_out([0, 1, 2, 3])
+    assert st == OK and len(pairs) == 3  # one host block per distinct GPU block
+    assert len(p.free) == free_before + 3
+    assert all(p.host_ref[h] == 4 for _, h in pairs)
+    st, back = p.swap_in([3, 2, 1, 0])
+    assert st == OK and len(back) == 3
+    assert all(p.ref[g] == 4 for _, g in back)
+    assert p.host_stats() == {"host_free": 12, "host_used": 0, "swapped": 0}
+    # the shared half-full block still copies on the first divergent append
+    st, slots, cow = p.append(1, 1)
+    assert st == OK and len(cow) == 1
+
+
+def test_swapping_part_of_a_family_unshares_only_the_swapped_one():
+    p = PoolModel(12, 4)
+    p.set_host_blocks(12)
+    p.create(0)
+    p.append(0, 8)
+    p.fork(0, 1)
+    st, pairs = p.swap_out([1])
+    assert st == OK and len(pairs) == 2
+    assert [p.ref[b] for b in p.tables[0]] == [1, 1]   # 0 keeps its blocks
+    st, back = p.swap_in([1])
+    assert st == OK
+    assert set(p.tables[1]).isdisjoint(p.tables[0])    # private copies now
+    assert p.stats()["shared"] == 0
+
+
+def test_swap_no_blocks_leaves_everything_unchanged():
+    p = PoolModel(6, 4, [4, 0, 5, 1, 3, 2])
+    p.set_host_blocks(2)
+    p.create(0)
+    p.append(0, 12)
+    snap = (list(p.free), list(p.ref), list(p.host_free), list(p.host_ref),
+            {s: list(t) for s, t in p.tables.items()}, set(p.swapped))
+    assert p.swap_out([0]) == (NO_BLOCKS, [])
+    assert snap == (list(p.free), list(p.ref), list(p.host_free), list(p.host_ref),
+                    {s: list(t) for s, t in p.tables.items()}, set(p.swapped))
+    assert p.swap_in([0]) == (INVALID, [])
+    assert p.swap_out([0, 9]) == (UNKNOWN_SEQ, [])

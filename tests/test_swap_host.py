@@ -1,0 +1,150 @@
+"""Swapping whole sequences to host blocks and back: the C++ pool against the
+pool model (bit exact), error paths, all-or-nothing behaviour.  No GPU."""
+import os
+import random
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_12_amd as pa
+from oracle.pool_model import PoolModel
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pa.LIB_PATH):
+        pytest.skip("libpa.so not built")
+    return pa.lib()
+
+
+def compare(pool, model):
+    assert pool.free_list().tolist() == list(model.free)
+    for b in range(model.num_blocks):
+        assert pool.refcount(b) == model.ref[b]
+    for sid, t in model.tables.items():
+        got, n = pool.block_table(sid)
+        assert got.tolist() == t and n == model.fill[sid]
+        assert pool.is_swapped(sid) == (1 if sid in model.swapped else 0)
+    assert pool.stats() == model.stats()
+    assert pool.host_stats() == model.host_stats()
+
+
+@pytest.mark.parametrize("seed,bs,H", [(11, 16, 300), (12, 32, 40), (13, 4, 120)])
+def test_swap_fuzz_bit_exact_against_model(L, seed, bs, H):
+    rng = random.Random(seed)
+    N = 193
+    order = rng.sample(range(N), N)
+    pool, model = pa.Pool(N, bs, order), PoolModel(N, bs, order)
+    assert pool.set_host_blocks(H) == model.set_host_blocks(H) == pa.PA_OK
+    live, nxt = [], 0
+    for it in range(3000):
+        r = rng.random()
+        on_gpu = [s for s in live if s not in model.swapped]
+        off = [s for s in live if s in model.swapped]
+        if r < 0.08 or not live:
+            assert pool.create(nxt) == model.create(nxt); live.append(nxt); nxt += 1
+        elif r < 0.15:
+            p = rng.choice(live)
+            assert pool.fork(p, nxt) == model.fork(p, nxt)
+            if nxt in model.tables:
+                live.append(nxt)
+            nxt += 1
+        elif r < 0.21:
+            s = rng.choice(live); live.remove(s)
+            assert pool.free(s) == model.free_seq(s)
+        elif r < 0.31:
+            # swap out a batch (sometimes mixing in a swapped or unknown id)
+            sids = rng.sample(live, min(len(live), rng.randint(1, 5)))
+            if rng.random() < 0.1:
+                sids.append(10 ** 9)
+            s1, p1 = pool.swap_out(sids)
+            s2, p2 = model.swap_out(sids)
+            assert s1 == s2
+            assert [tuple(x) for x in p1.tolist()] == p2
+        elif r < 0.41:
+            sids = rng.sample(live, min(len(live), rng.randint(1, 5)))
+            if off and rng.random() < 0.7:
+                sids = rng.sample(off, min(len(off), rng.randint(1, 4)))
+            s1, p1 = pool.swap_in(sids)
+            s2, p2 = model.swap_in(sids)
+            assert s1 == s2
+            assert [tuple(x) for x in p1.tolist()] == p2
+        else:
+            sids = rng.sample(live, min(len(live), rng.randint(1, 6)))
+            k = rng.choice([1, 1, 2, 5, bs, 2 * bs + 1])
+            s1, sl1, pr1 = pool.append_batch(sids, k)
+            s2, sl2, pr2 = model.append_batch(sids, k)
+            assert s1 == s2
+            assert sl1.tolist() == sl2
+            assert [tuple(x) for x in pr1.tolist()] == pr2
+        if it % 40 == 0:
+            compare(pool, model)
+    compare(pool, model)
+
+
+def test_swap_error_paths(L):
+    pool = pa.Pool(16, 16)
+    assert pool.set_host_blocks(8) == pa.PA_OK
+    for s in (0, 1):
+        pool.create(s)
+        pool.append(s, 20)
+    assert pool.swap_out([0, 0])[0] == pa.PA_ERR_INVALID          # repeated id
+    assert pool.swap_out([0, 77])[0] == pa.PA_ERR_UNKNOWN_SEQ
+    assert pool.swap_in([0])[0] == pa.PA_ERR_INVALID              # not swapped
+    assert pool.swap_out([0], cap=1)[0] == pa.PA_ERR_INVALID      # two blocks, cap 1
+    st, pairs = pool.swap_out([0])
+    assert st == pa.PA_OK and pairs.shape == (2, 2)
+    assert pool.is_swapped(0) == 1 and pool.is_swapped(1) == 0 and pool.is_swapped(5) == -1
+    # a swapped sequence takes no appends, forks or decode tables
+    assert pool.append(0, 1)[0] == pa.PA_ERR_INVALID
+    assert pool.append_batch([1, 0], 1)[0] == pa.PA_ERR_INVALID
+    assert pool.fork(0, 9) == pa.PA_ERR_INVALID
+    with pytest.raises(pa.PAError):
+        pool.block_tables([0, 1], 4)
+    assert pool.swap_out([0])[0] == pa.PA_ERR_INVALID             # already swapped
+    assert pool.swap_in([0, 77])[0] == pa.PA_ERR_UNKNOWN_SEQ
+    assert pool.set_host_blocks(4) == pa.PA_ERR_INVALID           # host area in use
+    # free of a swapped sequence releases its host blocks
+    assert pool.free(0) == pa.PA_OK
+    assert pool.host_stats() == {"host_free": 8, "host_used": 0, "swapped": 0}
+    assert pool.set_host_blocks(4) == pa.PA_OK
+    L = pa.lib()
+    assert L.pa_seq_swap_out(None, None, 0, None, 0, None) == pa.PA_ERR_INVALID
+    assert L.pa_seq_swap_in(pool._h, None, -1, None, 0, None) == pa.PA_ERR_INVALID
+    assert L.pa_pool_host_stats(pool._h, None) == pa.PA_ERR_INVALID
+    assert L.pa_seq_is_swapped(None, 0) == -1
+
+
+def test_swap_is_all_or_nothing(L):
+    pool = pa.Pool(8, 16, [5, 2, 7, 0, 1, 3, 6, 4])
+    pool.set_host_blocks(3)
+    for s in (0, 1):
+        pool.create(s)
+        pool.append(s, 33)                 # 3 blocks each
+    pool.fork(0, 2)
+
+    def state():
+        return (pool.free_list().tolist(), pool.stats(), pool.host_stats(),
+                [pool.refcount(b) for b in range(8)],
+                [pool.block_table(s)[0].tolist() for s in (0, 1, 2)])
+
+    before = state()
+    assert pool.swap_out([0, 1])[0] == pa.PA_ERR_NO_BLOCKS   # 6 distinct blocks > 3
+    assert state() == before
+    # 0 and its fork 2 share all three blocks: one host block each, refcount 2
+    st, pairs = pool.swap_out([0, 2])
+    assert st == pa.PA_OK and len(pairs) == 3
+    assert pool.host_stats() == {"host_free": 0, "host_used": 3, "swapped": 2}
+    assert pool.free_list().tolist()[-3:] == pairs[:, 0].tolist()   # released in order
+    # fill the GPU so that swap-in cannot fit, then check nothing moves
+    pool.create(3)
+    pool.append(3, 16 * pool.stats()["free"])
+    before = (pool.free_list().tolist(), pool.stats(), pool.host_stats())
+    assert pool.swap_in([0, 2])[0] == pa.PA_ERR_NO_BLOCKS
+    assert (pool.free_list().tolist(), pool.stats(), pool.host_stats()) == before
+    pool.free(3)
+    st, back = pool.swap_in([2, 0])
+    assert st == pa.PA_OK and len(back) == 3
+    t0, t2 = pool.block_table(0)[0].tolist(), pool.block_table(2)[0].tolist()
+    assert t0 == t2 and all(pool.refcount(b) == 2 for b in t0)      # still shared
+    assert pool.stats()["shared"] == 3
