@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--swap", action="store_true",
                     help="measure swapping half of the workload's sequences out to pinned "
                          "host memory and back (pa_seq_swap_out/in + pa_swap_blocks)")
+    ap.add_argument("--prefix", action="store_true",
+                    help="measure prefix reuse (chain hashing and radix tree) on a shared "
+                         "system-prompt request stream (host only)")
     ap.add_argument("--calibrate", action="store_true",
                     help="run only a 1 GiB device copy and fill of known size (for scaling "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -310,6 +313,77 @@ def bench_swap(args):
     print(json.dumps(res), flush=True)
 
 
+def prefix_stream(seed: int = 105, n_req: int = 256, prefix: int = 4096, bs: int = 16):
+    """Requests of the shared-prefix workload as token ids: one 4096-token
+    system prompt, then U{64..1024} private tokens per request."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(9,))))
+    system = g.integers(0, 32000, prefix).astype(np.int32)
+    lens = g.integers(64, 1024, n_req, endpoint=True)
+    return [np.concatenate([system, g.integers(0, 32000, int(n)).astype(np.int32)])
+            for n in lens]
+
+
+def bench_prefix(args):
+    """Host cost of prefix reuse: every request of the stream through
+    pa_seq_create_cached (lookup, allocation, indexing of its new blocks),
+    for each index kind; the oracle's model on a bounded sample beside it."""
+    import paged_kv_cache_12_amd as pa
+    from oracle.pool_model import PoolModel
+    bs = 16
+    reqs = prefix_stream(bs=bs)
+    blocks = sum(-(-len(r) // bs) for r in reqs)
+    res = {"metric": "prefix reuse on the host: microseconds per request (create with lookup) "
+                     "and hit rate",
+           "unit": "us/request", "higher_is_better": False, "data": "synthetic token ids",
+           "config": {"workload": "shared 4096-token system prompt + U{64..1024} private tokens",
+                      "requests": len(reqs), "block_size": bs,
+                      "prompt_tokens": int(sum(len(r) for r in reqs))}}
+    # one core's SHA-256 rate: the bound for the hashing index
+    buf = np.random.default_rng(0).integers(0, 256, 64 << 20, dtype=np.uint8).tobytes()
+    t0 = time.perf_counter()
+    pa.sha256(buf)
+    sha_gbs = len(buf) / (time.perf_counter() - t0) / 1e9
+    for kind, name in ((pa.PA_PREFIX_HASH, "hash"), (pa.PA_PREFIX_RADIX, "radix")):
+        per = []
+        for rep in range(max(1, min(args.steps, 5))):
+            pool = pa.Pool(blocks + 64, bs)
+            pool.enable_prefix_cache(kind)
+            t0 = time.perf_counter()
+            for i, r in enumerate(reqs):
+                st, cached, _ = pool.create_cached(i, r)
+                assert st == 0
+            per.append((time.perf_counter() - t0) / len(reqs) * 1e6)
+        stats = pool.prefix_stats()
+        us = float(np.median(per))
+        res[name] = {"us_per_request": round(us, 2),
+                     "hit_rate_blocks": round(stats["hits"] / max(1, stats["queried"]), 4),
+                     "cached_tokens_last_request": int(cached),
+                     "indexed_blocks": stats["indexed"], "nodes": stats["nodes"]}
+        if kind == pa.PA_PREFIX_HASH:
+            hashed = sum(len(r) // bs * (bs * 4 + 44) for r in reqs)   # bytes hashed per block
+            res[name]["hash_GBps"] = round(hashed / (us * 1e-6 * len(reqs)) / 1e9, 3)
+            res[name]["roofline"] = {"bound": "host sha256", "achieved":
+                                     res[name]["hash_GBps"], "peak": round(sha_gbs, 3),
+                                     "unit": "GB/s", "frac": round(res[name]["hash_GBps"] /
+                                                                    sha_gbs, 4)}
+    # the oracle's models on the first 16 requests
+    sample = reqs[:16]
+    cpu = {}
+    for kind, name in ((1, "hash"), (2, "radix")):
+        m = PoolModel(blocks + 64, bs)
+        m.enable_prefix_cache(kind)
+        t0 = time.perf_counter()
+        for i, r in enumerate(sample):
+            m.create_cached(i, r.tolist())
+        cpu[name] = round((time.perf_counter() - t0) / len(sample) * 1e6, 1)
+    res["value"] = res["hash"]["us_per_request"]
+    res["cpu_baseline"] = {"value": cpu["hash"], "unit": "us/request", "cores": 1,
+                           "kind": "oracle", "radix_us_per_request": cpu["radix"],
+                           "sample": "the oracle's pool model with each index, first 16 "
+                                     "requests of the same stream"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -321,6 +395,9 @@ def main():
         return
     if args.swap:
         bench_swap(args)
+        return
+    if args.prefix:
+        bench_prefix(args)
         return
     wl = synth.WORKLOADS[args.workload]
     part = wl.partition if args.partition is None else args.partition

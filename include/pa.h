@@ -340,6 +340,83 @@ int pa_seq_is_swapped(const pa_pool* pool, int64_t seq);
 /* stats_out[3] = {free host blocks, host blocks in use, swapped sequences}. */
 pa_status pa_pool_host_stats(const pa_pool* pool, int64_t* stats_out);
 
+/* ------------------------------------------------------------------------ */
+/* Prefix reuse (host memory only; no HIP calls)                              */
+/* ------------------------------------------------------------------------ */
+/*
+ * An index attached to the pool finds the blocks that already hold a
+ * request's prompt prefix, so only the rest is computed (aitalk.it,
+ * "RadixAttention: un albero che non dimentica" and the chain-hashing
+ * paragraph of "Due strati, non due rivali"; "KV Cache Administration",
+ * "How RadixAttention Works", "How vLLM Implements Prefix Caching", "Cache
+ * salting prevents cross-tenant reuse").  Both kinds give the same reuse when
+ * nothing is evicted; they differ in structure and eviction unit:
+ *
+ *   PA_PREFIX_HASH   key of block i = SHA-256(key of block i-1 (32 zero bytes
+ *                    for i = 0) ‖ LE32(block_size) ‖ token ids as LE32 ‖
+ *                    LE32(|e|) ‖ e), where e = LE32(|salt|) ‖ salt ‖ extra
+ *                    for block 0 and e = extra after it (pa_prefix_block_hash).
+ *                    Eviction: single blocks, least recently idle first,
+ *                    deepest first among blocks idle since the same call.
+ *   PA_PREFIX_RADIX  compressed trie over token ids at block granularity, one
+ *                    root per (salt, extra).  Eviction: whole leaves no
+ *                    sequence holds or sits in, least recently used first
+ *                    (deeper first among equals); inner nodes go only after
+ *                    all their children.
+ *
+ * The index holds one reference on every block it indexes, so a cached block
+ * outlives its requests; it is evicted only when an allocation finds the free
+ * list short (pa_pool_stats counts it as used; "shared" counts sequence
+ * references only).  Only full blocks are indexed.  A block is indexed as
+ * soon as it is full: its K/V must be written (pa_write_kv on the slots
+ * returned) before work that reads a later request's hits, which in-order
+ * use of one stream gives.
+ */
+enum { PA_PREFIX_HASH = 1, PA_PREFIX_RADIX = 2 };
+
+/* SHA-256 (FIPS 180-4) of data[0..len) into out[32]. */
+pa_status pa_sha256(const void* data, size_t len, uint8_t* out);
+
+/* Chain key of one block (see PA_PREFIX_HASH): parent[32] (NULL = zeros),
+ * tokens[n], extra[extra_len] -> out[32]. */
+pa_status pa_prefix_block_hash(const uint8_t* parent, const int32_t* tokens, int n,
+                               const void* extra, int extra_len, uint8_t* out);
+
+/* Attach an index of `kind` to a pool that has no sequences yet
+ * (PA_ERR_INVALID otherwise; PA_ERR_UNSUPPORTED for an unknown kind). */
+pa_status pa_pool_enable_prefix_cache(pa_pool* pool, int kind);
+
+/*
+ * New sequence for a prompt tokens[0..n): the longest run of its full blocks
+ * that ends before its last token and is found in the index is mapped (no K/V
+ * to compute; *cached_tokens_out = that run's tokens, a multiple of
+ * block_size), fresh blocks are taken for the rest, and slots_out
+ * [n - cached] receives the slots of tokens cached..n-1 for pa_write_kv.
+ * The new full blocks are indexed.  salt (tenant) and extra (for example an
+ * adapter id) are part of every key: different salts never share blocks.
+ * All or nothing: PA_ERR_NO_BLOCKS (nothing changes, not even recency) when
+ * free plus evictable blocks cannot cover the new blocks; PA_ERR_INVALID
+ * without an index or for an existing id.
+ */
+pa_status pa_seq_create_cached(pa_pool* pool, int64_t seq, const int32_t* tokens, int n,
+                               const void* salt, int salt_len, const void* extra, int extra_len,
+                               int* cached_tokens_out, int64_t* slots_out);
+
+/*
+ * pa_seq_append_batch with token ids tokens[n][tokens_each]: a sequence
+ * created by pa_seq_create_cached keeps feeding the index, which indexes each
+ * block as it fills.  Plain pa_seq_append_batch, pa_seq_swap_out and
+ * pa_seq_free end that tracking for a sequence; pa_seq_fork passes it on.
+ */
+pa_status pa_seq_append_tokens(pa_pool* pool, const int64_t* seqs, int n, const int32_t* tokens,
+                               int tokens_each, int64_t* slots_out, int32_t* pairs_out,
+                               int* num_pairs_out);
+
+/* stats_out[6] = {indexed blocks, blocks eviction could free now, blocks
+ * found (cumulative), blocks looked up (cumulative), blocks evicted
+ * (cumulative), tree nodes (radix; 0 for hash)}; all 0 without an index. */
+pa_status pa_prefix_stats(const pa_pool* pool, int64_t* stats_out);
+
 /* Copy seq's block table into out[0..cap); *num_blocks_out, *num_tokens_out get
  * its length and fill.  PA_ERR_INVALID if cap is too small (nothing copied). */
 pa_status pa_seq_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int cap,

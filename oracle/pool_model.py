@@ -43,6 +43,11 @@ preempted sequence comes back by swapping in or by recomputing).  Readings:
     references released in order; pairs (host, gpu);
   * a swapped sequence cannot be appended to, forked or decoded; freeing it
     (the recompute choice) releases its host blocks.
+
+Prefix reuse (oracle/prefix_cache.py): an index may hold one reference on a
+full block; "shared" and copy-on-write count sequence references only; when
+an allocation finds the free list short the index evicts blocks only it
+holds (all-or-nothing checks count them as available).
 """
 from __future__ import annotations
 
@@ -68,6 +73,34 @@ class PoolModel:
         self.swapped: set[int] = set()
         self.host_free = deque()
         self.host_ref: list[int] = []
+        self.idx = [0] * num_blocks        # 1 if the prefix index holds the block
+        self.index = None
+        self.tick = 0
+        self.track: dict[int, object] = {}  # tracking state of sequences (prefix reuse)
+
+    def seq_refs(self, b: int) -> int:
+        return self.ref[b] - self.idx[b]
+
+    def _retain(self, b: int):
+        self.ref[b] += 1
+        if self.idx[b] and self.seq_refs(b) == 1:
+            self.index.on_busy(b)
+
+    def _ensure(self, need: int) -> bool:
+        if need <= len(self.free):
+            return True
+        if self.index is None or len(self.free) + self.index.evictable([]) < need:
+            return False
+        self.index.evict(need - len(self.free))
+        return need <= len(self.free)
+
+    def _untrack(self, sid):
+        t = self.track.get(sid)
+        if t is not None and t.tracked:
+            self.index.untrack(sid, t)
+        if t is not None:
+            t.tracked = False
+            t.pending = []
 
     def set_host_blocks(self, n: int) -> int:
         if n < 0 or self.swapped:
@@ -80,12 +113,15 @@ class PoolModel:
     def _alloc(self) -> int:
         b = self.free.popleft()
         self.ref[b] = 1
+        self.idx[b] = 0
         return b
 
     def _release(self, b: int):
         self.ref[b] -= 1
         if self.ref[b] == 0:
             self.free.append(b)
+        elif self.idx[b] and self.seq_refs(b) == 0:
+            self.index.on_idle(b)
 
     # -- sequence operations -------------------------------------------------
     def create(self, sid: int) -> int:
@@ -103,12 +139,19 @@ class PoolModel:
         self.tables[child] = list(self.tables[parent])
         self.fill[child] = self.fill[parent]
         for b in self.tables[child]:
-            self.ref[b] += 1
+            self._retain(b)
+        if parent in self.track:
+            self.track[child] = self.track[parent].copy()
+            if self.track[child].tracked:
+                self.index.on_fork(child, self.track[child])
         return OK
 
     def free_seq(self, sid: int) -> int:
+        self.tick += 1
         if sid not in self.tables:
             return UNKNOWN_SEQ
+        self._untrack(sid)
+        self.track.pop(sid, None)
         if sid in self.swapped:
             self.swapped.discard(sid)
             for h in self.tables.pop(sid):
@@ -145,6 +188,7 @@ class PoolModel:
 
     def swap_out(self, sids):
         """Returns (status, pairs [(gpu, host), ...])."""
+        self.tick += 1
         st = self._batch_ok(sids, False)
         if st != OK:
             return st, []
@@ -152,6 +196,8 @@ class PoolModel:
         if len(blocks) > len(self.host_free):
             return NO_BLOCKS, []
         to_host = {b: self.host_free.popleft() for b in blocks}
+        for s in sids:
+            self._untrack(s)
         for s in sids:
             new = []
             for b in self.tables[s]:
@@ -164,25 +210,53 @@ class PoolModel:
 
     def swap_in(self, sids):
         """Returns (status, pairs [(host, gpu), ...])."""
+        self.tick += 1
         st = self._batch_ok(sids, True)
         if st != OK:
             return st, []
         hosts = self._distinct(sids)
-        if len(hosts) > len(self.free):
+        if not self._ensure(len(hosts)):
             return NO_BLOCKS, []
         to_gpu = {}
+        first = {}
         for h in hosts:
-            to_gpu[h] = self.free.popleft()
-            self.ref[to_gpu[h]] = 0
+            to_gpu[h] = self._alloc()
+            first[h] = True
         for s in sids:
             new = []
             for h in self.tables[s]:
-                self.ref[to_gpu[h]] += 1
+                if first[h]:
+                    first[h] = False
+                else:
+                    self._retain(to_gpu[h])
                 self._host_release(h)
                 new.append(to_gpu[h])
             self.tables[s] = new
             self.swapped.discard(s)
         return OK, [(h, to_gpu[h]) for h in hosts]
+
+    # -- prefix reuse (oracle/prefix_cache.py) -----------------------------------
+    def _release_index_ref(self, b: int):
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self.free.append(b)
+
+    def enable_prefix_cache(self, kind: int) -> int:
+        from . import prefix_cache
+        return prefix_cache.enable(self, kind)
+
+    def create_cached(self, sid: int, tokens, salt: bytes = b"", extra: bytes = b""):
+        from . import prefix_cache
+        return prefix_cache.create_cached(self, sid, tokens, salt, extra)
+
+    def append_tokens(self, sids, tokens):
+        return self.append_batch(list(sids), len(tokens[0]) if len(sids) else 0, tokens)
+
+    def prefix_stats(self):
+        if self.index is None:
+            return {"indexed": 0, "evictable": 0, "hits": 0, "queried": 0, "evicted": 0,
+                    "nodes": 0}
+        return self.index.stats()
 
     def host_stats(self):
         return {"host_free": len(self.host_free),
@@ -199,13 +273,16 @@ class PoolModel:
             need += 1
         return need
 
+    def _seq_ref_view(self):
+        return _SeqRefs(self)
+
     def _append_one_call(self, sid: int, k: int, slots: list, pairs: list):
         table = self.tables[sid]
         for j in range(k):
             n = self.fill[sid]
             if n % self.bs == 0:
                 table.append(self._alloc())
-            elif j == 0 and self.ref[table[-1]] > 1:
+            elif j == 0 and self.seq_refs(table[-1]) > 1:
                 old = table[-1]
                 new = self._alloc()
                 pairs.append((old, new))
@@ -219,31 +296,53 @@ class PoolModel:
         """Returns (status, slots, pairs)."""
         return self.append_batch([sid], k)
 
-    def append_batch(self, sids, k: int):
+    def append_batch(self, sids, k: int, tokens=None):
         """Append k tokens to each sequence of `sids`, in order.  Returns
-        (status, slots [len(sids)*k], pairs [(src, dst), ...])."""
+        (status, slots [len(sids)*k], pairs [(src, dst), ...]).  tokens
+        [len(sids)][k] (token ids) keep a tracked sequence feeding the prefix
+        index; without them its tracking ends."""
         if k < 0:
             return INVALID, [], []
+        self.tick += 1
         for s in sids:
             if s not in self.tables:
                 return UNKNOWN_SEQ, [], []
         if any(s in self.swapped for s in sids) or len(set(sids)) != len(sids):
             return INVALID, [], []
+        if k == 0 or not sids:
+            return OK, [], []
         # dry run of the refcount changes to count the blocks the batch takes
         ref = {}
         need = 0
+        seq_ref = self._seq_ref_view()
         for s in sids:
-            view = _RefView(self.ref, ref)
+            view = _RefView(seq_ref, ref)
             c = self._needed(s, k, view)
             need += c
             n = self.fill[s]
             if k and n % self.bs != 0 and view[self.tables[s][-1]] > 1:
                 ref[self.tables[s][-1]] = view[self.tables[s][-1]] - 1
-        if need > len(self.free):
+        if not self._ensure(need):
             return NO_BLOCKS, [], []
         slots, pairs = [], []
-        for s in sids:
+        for i, s in enumerate(sids):
+            first = self.fill[s]
+            start = len(slots)
             self._append_one_call(s, k, slots, pairs)
+            if tokens is None:
+                self._untrack(s)
+                continue
+            t = self.track.get(s)
+            if t is None or not t.tracked:
+                continue
+            for j in range(k):
+                if not t.tracked:
+                    break
+                t.pending.append(int(tokens[i][j]))
+                if len(t.pending) == self.bs:
+                    self.index.add_full_block(s, t, slots[start + j] // self.bs,
+                                              (first + j) // self.bs, t.pending)
+                    t.pending = []
         return OK, slots, pairs
 
     # -- queries -------------------------------------------------------------
@@ -252,10 +351,18 @@ class PoolModel:
 
     def stats(self):
         used = sum(1 for r in self.ref if r > 0)
-        shared = sum(1 for r in self.ref if r > 1)
+        shared = sum(1 for b in range(self.num_blocks) if self.seq_refs(b) > 1)
         tokens = sum(self.fill.values())
         return {"free": len(self.free), "used": used, "shared": shared,
                 "tokens": tokens, "copies": self.copies}
+
+
+class _SeqRefs:
+    def __init__(self, pool):
+        self.pool = pool
+
+    def __getitem__(self, b):
+        return self.pool.seq_refs(b)
 
 
 class _RefView:

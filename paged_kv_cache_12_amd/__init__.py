@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libpa.so")
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_UNKNOWN_SEQ, PA_ERR_HIP = range(6)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_DECODE_SHARED_KV = 1
+PA_PREFIX_HASH, PA_PREFIX_RADIX = 1, 2
 DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
 
 # name -> (restype, argtypes), mirroring include/pa.h
@@ -44,6 +45,12 @@ SIGNATURES = {
     "pa_seq_swap_in": (_i, [_vp, _vp, _i, _vp, _i, _vp]),
     "pa_seq_is_swapped": (_i, [_vp, _i64]),
     "pa_pool_host_stats": (_i, [_vp, _vp]),
+    "pa_sha256": (_i, [_vp, _sz, _vp]),
+    "pa_prefix_block_hash": (_i, [_vp, _vp, _i, _vp, _i, _vp]),
+    "pa_pool_enable_prefix_cache": (_i, [_vp, _i]),
+    "pa_seq_create_cached": (_i, [_vp, _i64, _vp, _i, _vp, _i, _vp, _i, _vp, _vp]),
+    "pa_seq_append_tokens": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp]),
+    "pa_prefix_stats": (_i, [_vp, _vp]),
     "pa_decode_step_staging_size": (_sz, [_i, _i]),
     "pa_decode_step": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _f,
                             _i, _i, _vp, _vp, _sz, _vp, _sz, _i, _vp]),
@@ -290,6 +297,22 @@ def pa_decode_step(pool: "Pool", seqs: np.ndarray, k_new, v_new, k_cache, v_cach
     _check(st, "pa_decode_step")
 
 
+def sha256(data: bytes) -> bytes:
+    out = (ctypes.c_uint8 * 32)()
+    _check(lib().pa_sha256(data, len(data), out), "pa_sha256")
+    return bytes(out)
+
+
+def prefix_block_hash(parent, tokens, extra: bytes = b"") -> bytes:
+    """Chain key of one block: parent (32 bytes or None), token ids, extra bytes."""
+    tk = np.ascontiguousarray(tokens, dtype=np.int32)
+    out = (ctypes.c_uint8 * 32)()
+    par = None if parent is None else (ctypes.c_uint8 * 32).from_buffer_copy(parent)
+    _check(lib().pa_prefix_block_hash(par, _np_ptr(tk), tk.size, extra or None, len(extra), out),
+           "pa_prefix_block_hash")
+    return bytes(out)
+
+
 def pa_kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, dtype: int) -> int:
     return int(lib().pa_kv_bytes_per_token(num_layers, num_kv_heads, head_dim, dtype))
 
@@ -419,6 +442,42 @@ class Pool:
 
     def is_swapped(self, seq: int) -> int:
         return lib().pa_seq_is_swapped(self._h, seq)
+
+    # -- prefix reuse --------------------------------------------------------------
+    def enable_prefix_cache(self, kind: int) -> int:
+        return lib().pa_pool_enable_prefix_cache(self._h, kind)
+
+    def create_cached(self, seq: int, tokens, salt: bytes = b"", extra: bytes = b""):
+        """-> (status, cached_tokens, slots int64 [n - cached])."""
+        tk = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(max(1, tk.size), dtype=np.int64)
+        cached = ctypes.c_int(0)
+        st = lib().pa_seq_create_cached(self._h, seq, _np_ptr(tk), tk.size, salt or None,
+                                        len(salt), extra or None, len(extra),
+                                        ctypes.byref(cached), _np_ptr(slots))
+        if st != PA_OK:
+            return st, 0, slots[:0]
+        return st, cached.value, slots[:tk.size - cached.value]
+
+    def append_tokens(self, seqs, tokens):
+        """tokens [len(seqs)][k] -> (status, slots, pairs)."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        tk = np.ascontiguousarray(tokens, dtype=np.int32).reshape(seqs.size, -1)
+        n, k = seqs.size, tk.shape[1]
+        slots = np.empty(max(1, n * k), dtype=np.int64)
+        pairs = np.empty((max(1, n), 2), dtype=np.int32)
+        npairs = ctypes.c_int(0)
+        st = lib().pa_seq_append_tokens(self._h, _np_ptr(seqs), n, _np_ptr(tk), k, _np_ptr(slots),
+                                        _np_ptr(pairs), ctypes.byref(npairs))
+        if st != PA_OK:
+            return st, slots[:0], pairs[:0]
+        return st, slots[:n * k], pairs[:npairs.value]
+
+    def prefix_stats(self):
+        s = np.zeros(6, dtype=np.int64)
+        _check(lib().pa_prefix_stats(self._h, _np_ptr(s)), "pa_prefix_stats")
+        return dict(zip(("indexed", "evictable", "hits", "queried", "evicted", "nodes"),
+                        s.tolist()))
 
     def host_stats(self):
         s = np.zeros(3, dtype=np.int64)

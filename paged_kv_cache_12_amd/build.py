@@ -17,7 +17,7 @@ LIB = os.path.join(LIBDIR, "libpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("PA_ARCH", "gfx950")
 
-SOURCES = ["pa_pool.cpp", "pa_movement.hip", "pa_decode.hip", "pa_step.hip"]
+SOURCES = ["pa_pool.cpp", "pa_prefix.cpp", "pa_movement.hip", "pa_decode.hip", "pa_step.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -7,6 +7,8 @@
 // Each free list is a ring buffer holding each free block id once (FIFO: take
 // from the front, return to the back).  Sequences live in a hash map keyed by
 // the caller's 64-bit id.  Every operation is O(tokens + blocks touched).
+// Prefix indexes (chain hashing, radix tree) live in pa_prefix.cpp and attach
+// to the pool through the hooks in pa_pool_impl.h.
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
@@ -14,96 +16,11 @@
 #include <unordered_map>
 #include <vector>
 
-#include "../../include/pa.h"
+#include "pa_pool_impl.h"
 
-#define PA_EXPORT extern "C" __attribute__((visibility("default")))
-
-namespace {
-
-struct Seq {
-  std::vector<int32_t> table;  // GPU block ids, or host block ids when swapped
-  int64_t fill = 0;
-  bool swapped = false;
-};
-
-// FIFO of free block ids over [0, n)
-struct Ring {
-  std::vector<int32_t> buf;
-  int64_t head = 0, count = 0;
-  void init(int32_t n, const int32_t* order) {
-    buf.resize(n);
-    for (int32_t i = 0; i < n; ++i) buf[i] = order ? order[i] : i;
-    head = 0;
-    count = n;
-  }
-  int32_t pop() {
-    const int32_t b = buf[head];
-    head = (head + 1) % static_cast<int64_t>(buf.size());
-    --count;
-    return b;
-  }
-  void push(int32_t b) {
-    buf[(head + count) % static_cast<int64_t>(buf.size())] = b;
-    ++count;
-  }
-};
-
-}  // namespace
-
-struct pa_pool {
-  int32_t num_blocks = 0;
-  int32_t block_size = 0;
-  std::vector<int32_t> ring;  // free list storage, capacity num_blocks
-  int64_t head = 0;           // index of the front element
-  int64_t count = 0;          // number of free blocks
-  std::vector<int32_t> ref;
-  std::unordered_map<int64_t, Seq> seqs;
-  int64_t copies = 0;
-  int64_t tokens = 0;
-  int64_t shared = 0;  // blocks with refcount > 1
-  // host blocks for swapped sequences
-  Ring host;
-  std::vector<int32_t> host_ref;
-  int64_t host_used = 0;
-  int64_t swapped = 0;  // swapped sequences
-
-  int32_t alloc() {
-    int32_t b = ring[head];
-    head = (head + 1) % num_blocks;
-    --count;
-    ref[b] = 1;
-    return b;
-  }
-  void retain(int32_t b) {
-    if (++ref[b] == 2) ++shared;
-  }
-  void release(int32_t b) {
-    if (ref[b] == 2) --shared;
-    if (--ref[b] == 0) {
-      ring[(head + count) % num_blocks] = b;
-      ++count;
-    }
-  }
-  void host_release(int32_t h) {
-    if (--host_ref[h] == 0) {
-      host.push(h);
-      --host_used;
-    }
-  }
-};
+using namespace pa;
 
 namespace {
-
-// Blocks that appending k tokens to `s` takes, when the refcount of its last
-// block is `last_ref`.
-int64_t blocks_needed(const Seq& s, int64_t k, int32_t bs, int32_t last_ref) {
-  if (k <= 0) return 0;
-  const int64_t n = s.fill;
-  // positions n .. n+k-1 that start a block
-  int64_t need = (n + k + bs - 1) / bs - (n + bs - 1) / bs;
-  if (n % bs != 0 && last_ref > 1) need += 1;
-  return need;
-}
 
 void append_one(pa_pool* p, Seq& s, int64_t k, int64_t* slots, int32_t* pair, int* npairs) {
   const int32_t bs = p->block_size;
@@ -111,7 +28,7 @@ void append_one(pa_pool* p, Seq& s, int64_t k, int64_t* slots, int32_t* pair, in
     const int64_t n = s.fill;
     if (n % bs == 0) {
       s.table.push_back(p->alloc());
-    } else if (j == 0 && p->ref[s.table.back()] > 1) {
+    } else if (j == 0 && p->seq_refs(s.table.back()) > 1) {
       const int32_t old = s.table.back();
       const int32_t nb = p->alloc();
       pair[0] = old;
@@ -137,8 +54,8 @@ PA_EXPORT pa_status pa_pool_create(int num_blocks, int block_size, const int32_t
   if (!p) return PA_ERR_INVALID;
   p->num_blocks = num_blocks;
   p->block_size = block_size;
-  p->ring.resize(num_blocks);
   p->ref.assign(num_blocks, 0);
+  p->idx.assign(num_blocks, 0);
   if (free_order) {
     std::vector<char> seen(num_blocks, 0);
     for (int i = 0; i < num_blocks; ++i) {
@@ -148,13 +65,9 @@ PA_EXPORT pa_status pa_pool_create(int num_blocks, int block_size, const int32_t
         return PA_ERR_INVALID;
       }
       seen[b] = 1;
-      p->ring[i] = b;
     }
-  } else {
-    for (int i = 0; i < num_blocks; ++i) p->ring[i] = i;
   }
-  p->head = 0;
-  p->count = num_blocks;
+  p->gpu.init(num_blocks, free_order);
   *out = p;
   return PA_OK;
 }
@@ -176,17 +89,25 @@ PA_EXPORT pa_status pa_seq_fork(pa_pool* p, int64_t parent, int64_t child) {
   Seq c = it->second;  // copy before emplace (rehash may move it)
   for (int32_t b : c.table) p->retain(b);
   p->tokens += c.fill;
-  p->seqs.emplace(child, std::move(c));
+  Seq& cs = p->seqs.emplace(child, std::move(c)).first->second;
+  if (cs.tracked && p->index) p->index->on_fork(*p, child, cs);
   return PA_OK;
 }
 
-PA_EXPORT pa_status pa_seq_append_batch(pa_pool* p, const int64_t* seqs, int n, int tokens_each,
-                                        int64_t* slots_out, int32_t* pairs_out,
-                                        int* num_pairs_out) {
+namespace pa {
+
+// Appends tokens_each positions to each sequence.  tokens (may be null) holds
+// their token ids [n][tokens_each]: a tracked sequence then feeds every block
+// it fills to the prefix index; without token ids a sequence stops being
+// tracked.
+pa_status append_batch_impl(pa_pool* p, const int64_t* seqs, int n, int tokens_each,
+                            const int32_t* tokens, int64_t* slots_out, int32_t* pairs_out,
+                            int* num_pairs_out) {
   if (!p || n < 0 || tokens_each < 0) return PA_ERR_INVALID;
   if (n > 0 && !seqs) return PA_ERR_INVALID;
   if (n > 0 && tokens_each > 0 && (!slots_out || !pairs_out)) return PA_ERR_INVALID;
   if (num_pairs_out) *num_pairs_out = 0;
+  ++p->tick;
   // resolve ids, reject duplicates
   std::vector<Seq*> ss(n);
   for (int i = 0; i < n; ++i) {
@@ -213,21 +134,55 @@ PA_EXPORT pa_status pa_seq_append_batch(pa_pool* p, const int64_t* seqs, int n, 
     if (!s.table.empty()) {
       last = s.table.back();
       auto o = overlay.find(last);
-      last_ref = (o == overlay.end()) ? p->ref[last] : o->second;
+      last_ref = (o == overlay.end()) ? p->seq_refs(last) : o->second;
     }
     need += blocks_needed(s, tokens_each, bs, last_ref);
     if (s.fill % bs != 0 && last_ref > 1) overlay[last] = last_ref - 1;
   }
-  if (need > p->count) return PA_ERR_NO_BLOCKS;
+  if (!p->ensure(need)) return PA_ERR_NO_BLOCKS;
   int np = 0;
   for (int i = 0; i < n; ++i) {
     int got = 0;
-    append_one(p, *ss[i], tokens_each, slots_out + static_cast<int64_t>(i) * tokens_each,
-               pairs_out + 2 * np, &got);
+    Seq& s = *ss[i];
+    int64_t* sl = slots_out + static_cast<int64_t>(i) * tokens_each;
+    append_one(p, s, tokens_each, sl, pairs_out + 2 * np, &got);
     np += got;
+    if (!tokens) {
+      p->untrack(seqs[i], s);
+      continue;
+    }
+    if (!s.tracked) continue;
+    const int32_t* tk = tokens + static_cast<int64_t>(i) * tokens_each;
+    const int64_t first = s.fill - tokens_each;
+    for (int j = 0; j < tokens_each && s.tracked; ++j) {
+      s.pending.push_back(tk[j]);
+      if (static_cast<int32_t>(s.pending.size()) == bs) {
+        p->index->add_full_block(*p, seqs[i], s, static_cast<int32_t>(sl[j] / bs),
+                                 (first + j) / bs, s.pending.data());
+        s.pending.clear();
+      }
+    }
   }
   if (num_pairs_out) *num_pairs_out = np;
   return PA_OK;
+}
+
+}  // namespace pa
+
+PA_EXPORT pa_status pa_seq_append_batch(pa_pool* p, const int64_t* seqs, int n, int tokens_each,
+                                        int64_t* slots_out, int32_t* pairs_out,
+                                        int* num_pairs_out) {
+  return append_batch_impl(p, seqs, n, tokens_each, nullptr, slots_out, pairs_out,
+                           num_pairs_out);
+}
+
+PA_EXPORT pa_status pa_seq_append_tokens(pa_pool* p, const int64_t* seqs, int n,
+                                         const int32_t* tokens, int tokens_each,
+                                         int64_t* slots_out, int32_t* pairs_out,
+                                         int* num_pairs_out) {
+  if (n > 0 && tokens_each > 0 && !tokens) return PA_ERR_INVALID;
+  return append_batch_impl(p, seqs, n, tokens_each, tokens, slots_out, pairs_out,
+                           num_pairs_out);
 }
 
 PA_EXPORT pa_status pa_seq_append(pa_pool* p, int64_t seq, int num_tokens, int64_t* slots_out,
@@ -237,8 +192,10 @@ PA_EXPORT pa_status pa_seq_append(pa_pool* p, int64_t seq, int num_tokens, int64
 
 PA_EXPORT pa_status pa_seq_free(pa_pool* p, int64_t seq) {
   if (!p) return PA_ERR_INVALID;
+  ++p->tick;
   auto it = p->seqs.find(seq);
   if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+  p->untrack(seq, it->second);
   if (it->second.swapped) {
     for (int32_t h : it->second.table) p->host_release(h);
     --p->swapped;
@@ -294,10 +251,10 @@ PA_EXPORT int pa_pool_refcount(const pa_pool* p, int32_t block) {
 
 PA_EXPORT pa_status pa_pool_free_list(const pa_pool* p, int32_t* out, int cap, int* n_out) {
   if (!p || cap < 0) return PA_ERR_INVALID;
-  if (n_out) *n_out = static_cast<int>(p->count);
-  if (p->count > cap) return PA_ERR_INVALID;
-  if (p->count && !out) return PA_ERR_INVALID;
-  for (int64_t i = 0; i < p->count; ++i) out[i] = p->ring[(p->head + i) % p->num_blocks];
+  if (n_out) *n_out = static_cast<int>(p->gpu.count);
+  if (p->gpu.count > cap) return PA_ERR_INVALID;
+  if (p->gpu.count && !out) return PA_ERR_INVALID;
+  for (int64_t i = 0; i < p->gpu.count; ++i) out[i] = p->gpu.at(i);
   return PA_OK;
 }
 
@@ -305,7 +262,7 @@ PA_EXPORT pa_status pa_pool_stats(const pa_pool* p, int64_t* stats_out) {
   if (!p || !stats_out) return PA_ERR_INVALID;
   int64_t used = 0;
   for (int32_t r : p->ref) used += r > 0;
-  stats_out[0] = p->count;
+  stats_out[0] = p->gpu.count;
   stats_out[1] = used;
   stats_out[2] = p->shared;
   stats_out[3] = p->tokens;
@@ -362,6 +319,7 @@ void distinct_blocks(const std::vector<Seq*>& ss, std::vector<int32_t>& uniq,
 PA_EXPORT pa_status pa_seq_swap_out(pa_pool* p, const int64_t* seqs, int n, int32_t* pairs_out,
                                     int cap, int* num_pairs_out) {
   if (!p || cap < 0) return PA_ERR_INVALID;
+  ++p->tick;
   if (num_pairs_out) *num_pairs_out = 0;
   std::vector<Seq*> ss;
   pa_status st = resolve_batch(p, seqs, n, false, ss);
@@ -379,6 +337,7 @@ PA_EXPORT pa_status pa_seq_swap_out(pa_pool* p, const int64_t* seqs, int n, int3
     pairs_out[2 * i + 1] = hb[i];
   }
   p->host_used += k;
+  for (int i = 0; i < n; ++i) p->untrack(seqs[i], *ss[i]);
   for (Seq* s : ss) {
     for (int32_t& b : s->table) {
       const int32_t h = hb[slot[b]];
@@ -396,6 +355,7 @@ PA_EXPORT pa_status pa_seq_swap_out(pa_pool* p, const int64_t* seqs, int n, int3
 PA_EXPORT pa_status pa_seq_swap_in(pa_pool* p, const int64_t* seqs, int n, int32_t* pairs_out,
                                    int cap, int* num_pairs_out) {
   if (!p || cap < 0) return PA_ERR_INVALID;
+  ++p->tick;
   if (num_pairs_out) *num_pairs_out = 0;
   std::vector<Seq*> ss;
   pa_status st = resolve_batch(p, seqs, n, true, ss);
@@ -405,7 +365,7 @@ PA_EXPORT pa_status pa_seq_swap_in(pa_pool* p, const int64_t* seqs, int n, int32
   distinct_blocks(ss, uniq, slot);
   const int64_t k = static_cast<int64_t>(uniq.size());
   if (k > cap || (k > 0 && !pairs_out)) return PA_ERR_INVALID;
-  if (k > p->count) return PA_ERR_NO_BLOCKS;
+  if (!p->ensure(k)) return PA_ERR_NO_BLOCKS;
   std::vector<int32_t> gb(k);
   std::vector<char> first(k, 1);
   for (int64_t i = 0; i < k; ++i) {

@@ -128,6 +128,43 @@ class PagedKVCache:
                            self._pairs_to_device(pairs), stream=stream)
         return pairs
 
+    # -- prefix reuse -----------------------------------------------------------------
+    def enable_prefix_cache(self, kind: int):
+        st = self.pool.enable_prefix_cache(kind)
+        if st != PA_OK:
+            raise PAError(st, "pa_pool_enable_prefix_cache")
+
+    def create_cached(self, seq: int, tokens, k_of, v_of, salt: bytes = b"",
+                      extra: bytes = b"", stream=None):
+        """New sequence for prompt `tokens` through the prefix index; only the
+        positions not found in it are written: k_of(start, end) / v_of(start,
+        end) give their K/V as GPU tensors [end-start][H_kv][d].  Returns the
+        number of cached tokens."""
+        st, cached, slots = self.pool.create_cached(seq, tokens, salt, extra)
+        if st != PA_OK:
+            raise PAError(st, "pa_seq_create_cached")
+        n = len(tokens)
+        if n > cached:
+            ds = self.torch.from_numpy(np.ascontiguousarray(slots)).to(self.device)
+            pa_write_kv(k_of(cached, n), v_of(cached, n), self.k_cache, self.v_cache, ds,
+                        stream=stream)
+        return cached
+
+    def append_tokens(self, seqs, tokens, k_new, v_new, stream=None):
+        """append() with token ids [len(seqs)][k], so the prefix index keeps
+        indexing the blocks these sequences fill."""
+        torch = self.torch
+        st, slots, pairs = self.pool.append_tokens(np.asarray(seqs, dtype=np.int64), tokens)
+        if st != PA_OK:
+            raise PAError(st, "pa_seq_append_tokens")
+        if len(pairs):
+            dp = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device)
+            pa_copy_blocks(self.k_cache, self.v_cache, dp, stream=stream)
+        if len(slots):
+            ds = torch.from_numpy(np.ascontiguousarray(slots)).to(self.device)
+            pa_write_kv(k_new, v_new, self.k_cache, self.v_cache, ds, stream=stream)
+        return slots, pairs
+
     # -- append: pool slots, copy-on-write, block write ----------------------
     def append(self, seqs, k: int, k_new, v_new, stream=None):
         """Append k tokens to each sequence in `seqs` (in order).  k_new, v_new:

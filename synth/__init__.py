@@ -191,6 +191,23 @@ class Scenario:
         return k, v
 
 
+def prefix_values(tokens, start: int, end: int, heads: int, dim: int, dtype: str,
+                  seed: int = 0):
+    """K and V [end-start][heads][dim] for positions start..end-1 of a token
+    list, each drawn from a generator seeded by the token ids up to and
+    including that position (a rolling SHA-256), so equal prefixes give equal
+    values wherever they occur, as a model's K/V would."""
+    import hashlib
+    h = hashlib.sha256(seed.to_bytes(8, "little")).digest()
+    kv = np.empty((2, end - start, heads, dim), dtype=np.float32)
+    for pos in range(end):
+        h = hashlib.sha256(h + int(tokens[pos]).to_bytes(4, "little", signed=True)).digest()
+        if pos >= start:
+            g = np.random.Generator(np.random.PCG64(int.from_bytes(h[:8], "little")))
+            kv[:, pos - start] = g.standard_normal((2, heads, dim), dtype=np.float32)
+    return cast_storage(kv[0], dtype), cast_storage(kv[1], dtype)
+
+
 def _ceil_div(a, b):
     return -(-a // b)
 

@@ -1,0 +1,131 @@
+"""GPU parity for prefix reuse: request streams through the C++ pool's prefix
+index (chain hashing or radix tree) with the block write and the decode on the
+GPU, against the pool model and the oracle.  K/V of a position depend on the
+token ids up to it (synth.prefix_values), so a hit must carry exactly what the
+request would have written; caches bit-exact, attention within tolerance."""
+import random
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+import harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    import paged_kv_cache_12_amd as pa
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("kind,dtype,bs,part", [(1, "bf16", 16, 512), (2, "bf16", 16, 0),
+                                                (1, "f16", 32, 256), (2, "f32", 16, 512)])
+def test_prefix_stream_matches_oracle(kind, dtype, bs, part):
+    import torch
+    from oracle import attention as A
+    from oracle.pool_model import PoolModel
+    from paged_kv_cache_12_amd.manager import PagedKVCache, storage_to_torch, torch_to_storage
+    from test_gpu_parity import to_f64
+    say("prefix stream", "hash" if kind == 1 else "radix", dtype, bs, part)
+    rng = random.Random(kind * 10 + bs)
+    Hq, Hkv, d = (8, 2, 64) if dtype == "f32" else (16, 4, 128)
+    # pool sizes at which this stream both fits and evicts (checked on the model)
+    N = {(1, 16): 250, (2, 16): 220, (1, 32): 120, (2, 32): 120}[(kind, bs)]
+    order = np.random.default_rng(kind).permutation(N).astype(np.int32)
+    gpu = PagedKVCache(N, bs, Hkv, d, dtype, free_order=order, guard_blocks=1,
+                       fill_bits=synth.poison_bits(dtype))
+    gpu.enable_prefix_cache(kind)
+    model = PoolModel(N, bs, order)
+    model.enable_prefix_cache(kind)
+    st = synth.STORAGE[dtype]
+    kc = np.empty(A.k_cache_shape(N, Hkv, bs, d, dtype), st)
+    vc = np.empty(A.v_cache_shape(N, Hkv, bs, d, dtype), st)
+    ib = np.uint32 if dtype == "f32" else np.uint16
+    kc.view(ib)[...] = synth.poison_bits(dtype)
+    vc.view(ib)[...] = synth.poison_bits(dtype)
+    systems = [[rng.randrange(30000) for _ in range(rng.randint(150, 700))] for _ in range(3)]
+    toks, live, total_cached = {}, [], 0
+
+    def dev(a):
+        return storage_to_torch(a, dtype).cuda()
+
+    for sid in range(36):
+        base = rng.choice(systems)
+        t = base[:rng.randint(len(base) // 2, len(base))] + \
+            [rng.randrange(30000) for _ in range(rng.randint(1, 90))]
+        salt = b"other" if sid % 7 == 3 else b""
+        kv = {}
+
+        def k_of(a, b, t=t, kv=kv):
+            kv["k"], kv["v"] = synth.prefix_values(t, a, b, Hkv, d, dtype)
+            return dev(kv["k"])
+
+        def v_of(a, b, kv=kv):
+            return dev(kv["v"])
+
+        c = gpu.create_cached(sid, t, k_of, v_of, salt)
+        so, co, slots = model.create_cached(sid, t, salt)
+        assert so == 0 and co == c, (sid, c, co)
+        if len(slots):
+            A.write_kv(kc, vc, kv["k"], kv["v"], np.asarray(slots))
+        total_cached += c
+        toks[sid] = list(t)
+        live.append(sid)
+        if rng.random() < 0.3:                         # some finish: their blocks stay cached
+            f = live.pop(rng.randrange(len(live)))
+            gpu.free(f)
+            model.free_seq(f)
+        # a decode step with token ids for a few live sequences
+        step = rng.sample(live, min(len(live), 4))
+        new = [[rng.randrange(30000)] for _ in step]
+        if not step:
+            continue
+        ks, vs = [], []
+        for s_, nt in zip(step, new):
+            toks[s_] += nt
+            k1, v1 = synth.prefix_values(toks[s_], len(toks[s_]) - 1, len(toks[s_]), Hkv, d, dtype)
+            ks.append(k1)
+            vs.append(v1)
+        kk, vv = np.concatenate(ks), np.concatenate(vs)
+        sl_g, pr_g = gpu.append_tokens(step, new, dev(kk), dev(vv))
+        so, sl_o, pr_o = model.append_tokens(step, new)
+        assert so == 0 and sl_g.tolist() == sl_o and [tuple(x) for x in pr_g.tolist()] == pr_o
+        if pr_o:
+            A.copy_blocks(kc, vc, pr_o)
+        A.write_kv(kc, vc, kk, vv, np.asarray(sl_o))
+    torch.cuda.synchronize()
+    stats = gpu.pool.prefix_stats()
+    assert stats == model.prefix_stats()
+    say("  cached tokens", total_cached, stats)
+    assert total_cached > 0 and stats["evicted"] > 0
+    kf, vf = torch_to_storage(gpu.k_full, dtype), torch_to_storage(gpu.v_full, dtype)
+    assert np.array_equal(kf[1:1 + N].view(ib), kc.view(ib))
+    assert np.array_equal(vf[1:1 + N].view(ib), vc.view(ib))
+    # decode every live sequence
+    q = synth.normal_array(9, (kind, bs), (len(live), Hq, d), dtype)
+    out, tab, lens = gpu.decode(dev(q), live, 1.0 / np.sqrt(d), part)
+    torch.cuda.synchronize()
+    tab_o = np.full(tab.shape, -1, np.int32)
+    lens_o = np.zeros(len(live), np.int32)
+    for i, s_ in enumerate(live):
+        tb, n = model.block_table(s_)
+        tab_o[i, :len(tb)] = tb
+        lens_o[i] = n
+    assert np.array_equal(tab, tab_o) and np.array_equal(lens, lens_o)
+    ref = A.paged_decode(q, kc, vc, tab_o, lens_o, 1.0 / np.sqrt(d), dtype)
+    rows = list(range(len(live)))
+    ea, er = H.check_attention(to_f64(out, dtype), ref, dtype, rows)
+    say("  live", len(live), "max abs", ea, "max rel", er)

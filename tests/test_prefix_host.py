@@ -1,0 +1,158 @@
+"""Prefix reuse in the C++ pool against the oracle's models (bit exact):
+SHA-256 and block keys, then random request streams under eviction pressure
+mixing cached creation, appends with and without token ids, forks, frees and
+swaps, for both index kinds.  No GPU."""
+import hashlib
+import os
+import random
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_12_amd as pa
+from oracle.pool_model import PoolModel
+from oracle import prefix_cache as PC
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pa.LIB_PATH):
+        pytest.skip("libpa.so not built")
+    return pa.lib()
+
+
+def test_sha256_matches_hashlib(L):
+    rng = random.Random(0)
+    for n in [0, 1, 55, 56, 63, 64, 65, 119, 120, 1000, 4099]:
+        data = bytes(rng.randrange(256) for _ in range(n))
+        assert pa.sha256(data) == hashlib.sha256(data).digest()
+
+
+def test_portable_sha256_matches_hashlib(L):
+    # the path taken on CPUs without the SHA extensions, forced in a child
+    import subprocess
+    import sys
+    code = ("import hashlib, random, paged_kv_cache_12_amd as pa\n"
+            "rng = random.Random(2)\n"
+            "for n in list(range(0, 140)) + [1000, 4099]:\n"
+            "    d = bytes(rng.randrange(256) for _ in range(n))\n"
+            "    assert pa.sha256(d) == hashlib.sha256(d).digest(), n\n"
+            "print('ok')\n")
+    env = dict(os.environ, PA_SHA256_PORTABLE="1")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True,
+                         text=True, timeout=120)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stderr
+
+
+def test_block_key_matches_the_oracle(L):
+    rng = random.Random(1)
+    parent = None
+    for i in range(20):
+        toks = [rng.randrange(-2 ** 31, 2 ** 31) for _ in range(rng.choice([4, 16, 32]))]
+        extra = bytes(rng.randrange(256) for _ in range(rng.randint(0, 9)))
+        got = pa.prefix_block_hash(parent, toks, extra)
+        assert got == PC.block_key(parent, toks, extra)
+        parent = got
+
+
+def compare(pool, model):
+    assert pool.free_list().tolist() == list(model.free)
+    for b in range(model.num_blocks):
+        assert pool.refcount(b) == model.ref[b], b
+    for sid, t in model.tables.items():
+        got, n = pool.block_table(sid)
+        assert got.tolist() == t and n == model.fill[sid], sid
+    assert pool.stats() == model.stats()
+    assert pool.prefix_stats() == model.prefix_stats()
+    assert pool.host_stats() == model.host_stats()
+
+
+@pytest.mark.parametrize("kind,seed,bs", [(PC.HASH, 1, 4), (PC.HASH, 2, 16),
+                                          (PC.RADIX, 3, 4), (PC.RADIX, 4, 16),
+                                          (PC.HASH, 5, 8), (PC.RADIX, 6, 8)])
+def test_prefix_fuzz_bit_exact_against_model(L, kind, seed, bs):
+    rng = random.Random(seed)
+    N = 97
+    order = rng.sample(range(N), N)
+    pool, model = pa.Pool(N, bs, order), PoolModel(N, bs, order)
+    assert pool.enable_prefix_cache(kind) == model.enable_prefix_cache(kind) == 0
+    assert pool.set_host_blocks(64) == model.set_host_blocks(64) == 0
+    systems = [[rng.randrange(500) for _ in range(rng.randint(bs, 5 * bs))] for _ in range(3)]
+    history = []
+    live, nxt = [], 0
+    for it in range(1500):
+        r = rng.random()
+        if r < 0.25 or not live:
+            if history and rng.random() < 0.3:
+                toks = rng.choice(history) + [rng.randrange(500) for _ in range(rng.randint(1, 2 * bs))]
+            else:
+                base = rng.choice(systems)
+                toks = base[:rng.randint(0, len(base))] + \
+                    [rng.randrange(500) for _ in range(rng.randint(0, 3 * bs))]
+            salt = rng.choice([b"", b"", b"t"])
+            a = pool.create_cached(nxt, toks, salt)
+            b = model.create_cached(nxt, toks, salt)
+            assert a[0] == b[0] and a[1] == b[1] and a[2].tolist() == b[2], (it, a[:2], b[:2])
+            if a[0] == 0:
+                live.append(nxt)
+                history.append(toks)
+            nxt += 1
+        elif r < 0.37:
+            s = rng.choice(live); live.remove(s)
+            assert pool.free(s) == model.free_seq(s)
+        elif r < 0.45:
+            p = rng.choice(live)
+            assert pool.fork(p, nxt) == model.fork(p, nxt)
+            if nxt in model.tables:
+                live.append(nxt)
+            nxt += 1
+        elif r < 0.75:
+            sids = rng.sample(live, min(len(live), rng.randint(1, 3)))
+            k = rng.randint(1, 2 * bs)
+            tk = [[rng.randrange(500) for _ in range(k)] for _ in sids]
+            a = pool.append_tokens(sids, tk)
+            b = model.append_tokens(sids, tk)
+            assert a[0] == b[0] and a[1].tolist() == b[1]
+            assert [tuple(x) for x in a[2].tolist()] == b[2]
+        elif r < 0.8:
+            sids = rng.sample(live, min(len(live), rng.randint(1, 2)))
+            k = rng.randint(1, 3)
+            a, b = pool.append_batch(sids, k), model.append_batch(sids, k)
+            assert a[0] == b[0] and a[1].tolist() == b[1]
+        elif r < 0.9:
+            sids = rng.sample(live, min(len(live), rng.randint(1, 2)))
+            a, b = pool.swap_out(sids), model.swap_out(sids)
+            assert a[0] == b[0] and [tuple(x) for x in a[1].tolist()] == b[1]
+        else:
+            off = [s for s in live if s in model.swapped]
+            if off:
+                sids = rng.sample(off, min(len(off), 2))
+                a, b = pool.swap_in(sids), model.swap_in(sids)
+                assert a[0] == b[0] and [tuple(x) for x in a[1].tolist()] == b[1]
+        if it % 25 == 0:
+            compare(pool, model)
+    compare(pool, model)
+    st = model.prefix_stats()
+    assert st["hits"] > 0 and st["evicted"] > 0
+
+
+def test_prefix_error_paths(L):
+    p = pa.Pool(16, 4)
+    assert p.create_cached(0, [1, 2, 3])[0] == pa.PA_ERR_INVALID      # no index
+    assert p.enable_prefix_cache(9) == pa.PA_ERR_UNSUPPORTED
+    p.create(3)
+    assert p.enable_prefix_cache(pa.PA_PREFIX_HASH) == pa.PA_ERR_INVALID
+    q = pa.Pool(16, 4)
+    assert q.enable_prefix_cache(pa.PA_PREFIX_RADIX) == 0
+    assert q.enable_prefix_cache(pa.PA_PREFIX_HASH) == pa.PA_ERR_INVALID
+    assert q.create_cached(0, list(range(10)))[0] == 0
+    assert q.create_cached(0, [1])[0] == pa.PA_ERR_INVALID              # id exists
+    assert q.create_cached(1, list(range(100)))[0] == pa.PA_ERR_NO_BLOCKS
+    Lb = pa.lib()
+    assert Lb.pa_seq_create_cached(q._h, 5, None, 3, None, 0, None, 0, None, None) == pa.PA_ERR_INVALID
+    assert Lb.pa_seq_append_tokens(q._h, None, 1, None, 1, None, None, None) == pa.PA_ERR_INVALID
+    assert Lb.pa_prefix_stats(q._h, None) == pa.PA_ERR_INVALID
+    assert Lb.pa_sha256(None, 3, None) == pa.PA_ERR_INVALID
+    assert pa.Pool(4, 4).prefix_stats() == {"indexed": 0, "evictable": 0, "hits": 0,
+                                            "queried": 0, "evicted": 0, "nodes": 0}
