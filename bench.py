@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--swap", action="store_true",
                     help="measure swapping half of the workload's sequences out to pinned "
                          "host memory and back (pa_seq_swap_out/in + pa_swap_blocks)")
+    ap.add_argument("--beam", action="store_true",
+                    help="measure beam-search steps (fork / retire / append with batched "
+                         "copy-on-write, block write, decode) on the OPT-13B-class shapes")
     ap.add_argument("--prefix", action="store_true",
                     help="measure prefix reuse (chain hashing and radix tree) on a shared "
                          "system-prompt request stream (host only)")
@@ -384,6 +387,105 @@ def bench_prefix(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_beam(args, width: int = 4):
+    """Beam search on the OPT-13B-class shapes (fp16, 40 KV heads, d 128, block
+    16): 16 prompts of 1024 tokens, `width` beams each.  One step = one
+    pa_beam_decode_step over all beams (each new beam's parent drawn from its
+    prompt's beams): pool fork / retire / append, one staging copy,
+    pa_copy_blocks of the copy-on-write pairs, pa_write_kv of the new
+    positions, pa_decode of all beams."""
+    import torch
+    import paged_kv_cache_12_amd as pa
+    from paged_kv_cache_12_amd.manager import PagedKVCache
+    wl = synth.WORKLOADS["opt13b_sampling_fp16"]
+    P, plen, bs = wl.prompts, wl.prompt_len, wl.block_size
+    steps_total = args.warmup + args.steps
+    need = P * (-(-plen // bs)) + P * width * (steps_total // bs + 2)
+    dev = torch.device("cuda:0")
+    cache = PagedKVCache(need + 64, bs, wl.h_kv, wl.head_dim, wl.dtype, device=dev)
+    g = torch.Generator(device=dev).manual_seed(wl.seed)
+    for p in range(P):
+        cache.create(p)
+        kv = torch.randn((plen, wl.h_kv, wl.head_dim), generator=g, device=dev).half()
+        vv = torch.randn((plen, wl.h_kv, wl.head_dim), generator=g, device=dev).half()
+        cache.append([p], plen, kv, vv)
+    B = P * width
+    k_new = torch.randn((B, wl.h_kv, wl.head_dim), generator=g, device=dev).half()
+    v_new = torch.randn((B, wl.h_kv, wl.head_dim), generator=g, device=dev).half()
+    q = torch.randn((B, wl.h_q, wl.head_dim), generator=g, device=dev).half()
+    out = torch.empty_like(q)
+    rng = np.random.default_rng(wl.seed)
+    maxb = -(-(plen + steps_total + 1) // bs)
+    sbytes = pa.pa_decode_step_staging_size(B, maxb)
+    h_stage = [torch.empty(sbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    d_stage = torch.empty(sbytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(256, pa.pa_decode_workspace_size(B, wl.h_q, wl.head_dim,
+                                                          plen + steps_total + 1, wl.partition)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    done = [None, None]
+    beams = {p: [p] for p in range(P)}
+    nxt = [P]
+    copies = []
+    host_s = []
+    nsteps = [0]
+
+    def step():
+        olds, parents, news = [], [], []
+        for p in range(P):
+            olds += beams[p]
+            par = rng.choice(beams[p], size=width).tolist()
+            new = list(range(nxt[0], nxt[0] + width))
+            nxt[0] += width
+            parents += par
+            news += new
+            beams[p] = new
+        j = nsteps[0] & 1
+        nsteps[0] += 1
+        if done[j] is not None:
+            done[j].synchronize()          # staging buffer j is free again
+        h0 = time.perf_counter()
+        before = cache.pool.stats()["copies"]
+        pa.pa_beam_decode_step(cache.pool, olds, parents, news, k_new, v_new, cache.k_cache,
+                               cache.v_cache, q, out, wl.scale, wl.partition, maxb, h_stage[j],
+                               d_stage, ws)
+        host_s.append(time.perf_counter() - h0)
+        copies.append(cache.pool.stats()["copies"] - before)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        done[j] = ev
+        return news
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    copies.clear()
+    host_s.clear()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        live = step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    tab, lens = cache.tables(live)
+    e = 2
+    logical = float(lens.sum()) * 2 * wl.h_kv * wl.head_dim * e
+    unique = unique_kv_bytes(tab, lens, wl)
+    block_bytes = 2 * wl.h_kv * bs * wl.head_dim * e
+    res = {"metric": "beam-search decode steps: sequence-steps/s (fork, retire, append with "
+                     "copy-on-write, block write, decode)",
+           "value": round(B / (ms * 1e-3), 1), "unit": "seq-steps/s", "higher_is_better": True,
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "dtype": wl.dtype, "data": "synthetic",
+           "config": {"workload": "OPT-13B-class beam search", "prompts": P, "prompt_len": plen,
+                      "beam_width": width, "block_size": bs, "partition": wl.partition},
+           "cow_pairs_per_step": round(float(np.mean(copies)), 2),
+           "cow_bytes_per_step": round(float(np.mean(copies)) * 2 * block_bytes),
+           "kv_bytes_logical": round(logical), "kv_bytes_unique": round(unique),
+           "effective_unique_GBps": round(unique / (ms * 1e-3) / 1e9, 1),
+           "host_us_per_step": round(float(np.median(host_s)) * 1e6, 1)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -398,6 +500,9 @@ def main():
         return
     if args.prefix:
         bench_prefix(args)
+        return
+    if args.beam:
+        bench_beam(args)
         return
     wl = synth.WORKLOADS[args.workload]
     part = wl.partition if args.partition is None else args.partition

@@ -252,6 +252,26 @@ pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_seqs, const
                          size_t staging_bytes, void* workspace, size_t workspace_bytes,
                          int dtype, void* stream);
 
+/*
+ * pa_beam_decode_step — one beam-search iteration in one call:
+ * pa_seq_beam_step(old_beams, parents, new_beams) in the pool, then, as in
+ * pa_decode_step, the staging copy, pa_copy_blocks of its pairs, pa_write_kv of
+ * k_new / v_new (device [n_new][H_kv][d], in new_beams order) and pa_decode of
+ * q into out (device [n_new][H_q][d]).  Staging sized by
+ * pa_decode_step_staging_size(n_new, max_blocks_per_seq).  Shapes, buffers,
+ * table capacity and workspace are checked before the pool changes; the
+ * pool step's own rules (and its PA_ERR_NO_BLOCKS behaviour) are those of
+ * pa_seq_beam_step.  n_new == 0 retires the old beams and launches nothing.
+ */
+pa_status pa_beam_decode_step(pa_pool* pool, const int64_t* old_beams, int n_old,
+                              const int64_t* parents, const int64_t* new_beams, int n_new,
+                              const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              int num_blocks, int num_kv_heads, int head_dim, int block_size,
+                              const void* q, void* out, int num_q_heads, float scale,
+                              int partition_size, int max_blocks_per_seq, void* host_staging,
+                              void* dev_staging, size_t staging_bytes, void* workspace,
+                              size_t workspace_bytes, int dtype, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host block pool (host memory only; no HIP calls)                          */
 /* ------------------------------------------------------------------------ */
@@ -297,6 +317,27 @@ pa_status pa_seq_append_batch(pa_pool* pool, const int64_t* seqs, int n, int tok
 /* Release every block of seq in logical order (host blocks if it is swapped
  * out) and forget seq. */
 pa_status pa_seq_free(pa_pool* pool, int64_t seq);
+
+/*
+ * pa_seq_beam_step — one beam-search step (encyclopedia entry, "como
+ * funciona": beam candidates share intermediate blocks and the sharing
+ * pattern changes every step, like a process tree).  The new beams
+ * new_beams[j] become forks of parents[j] (each parent one of old_beams; a
+ * parent may have several children or none), then every old beam is freed
+ * (new ids may reuse old ids), then one position is appended to each new beam
+ * in the order given (pa_seq_append_batch, or pa_seq_append_tokens when
+ * tokens[n_new] is not NULL): slots_out [n_new], pairs_out [n_new][2] and
+ * *num_pairs_out are its copy-on-write pairs (run pa_copy_blocks before
+ * pa_write_kv).  Everything is checked before anything changes
+ * (PA_ERR_UNKNOWN_SEQ for an unknown old beam; PA_ERR_INVALID for a repeated,
+ * swapped or foreign id); the fork-and-retire part cannot fail after that.  If
+ * the append finds too few blocks it returns PA_ERR_NO_BLOCKS with the new
+ * beams in place and nothing appended.
+ */
+pa_status pa_seq_beam_step(pa_pool* pool, const int64_t* old_beams, int n_old,
+                           const int64_t* parents, const int64_t* new_beams, int n_new,
+                           const int32_t* tokens, int64_t* slots_out, int32_t* pairs_out,
+                           int* num_pairs_out);
 
 /*
  * Swapping whole sequences (encyclopedia entry, "como funciona": eviction

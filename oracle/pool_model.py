@@ -150,6 +150,10 @@ class PoolModel:
         self.tick += 1
         if sid not in self.tables:
             return UNKNOWN_SEQ
+        self._free_impl(sid)
+        return OK
+
+    def _free_impl(self, sid: int):
         self._untrack(sid)
         self.track.pop(sid, None)
         if sid in self.swapped:
@@ -234,6 +238,44 @@ class PoolModel:
             self.tables[s] = new
             self.swapped.discard(s)
         return OK, [(h, to_gpu[h]) for h in hosts]
+
+    # -- beam search (tonho.wtf "como funciona": beam candidates share blocks
+    # and the pattern changes every step) ----------------------------------------
+    def beam_step(self, olds, parents, news, tokens=None):
+        """New beams fork their parents (old beams), the old beams are freed,
+        then one position is appended to each new beam in order.  Returns
+        (status, slots, pairs).  Reading: the fork-and-retire part cannot fail
+        once checked; a short free list fails only the append."""
+        olds, parents, news = list(olds), list(parents), list(news)
+        for o in olds:
+            if o not in self.tables:
+                return UNKNOWN_SEQ, [], []
+        if any(o in self.swapped for o in olds) or len(set(olds)) != len(olds):
+            return INVALID, [], []
+        if len(set(news)) != len(news):
+            return INVALID, [], []
+        for par, nw in zip(parents, news):
+            if par not in olds or (nw in self.tables and nw not in olds):
+                return INVALID, [], []
+        self.tick += 1
+        kids = []
+        for par in parents:
+            table = list(self.tables[par])
+            for b in table:
+                self._retain(b)
+            tr = self.track[par].copy() if par in self.track else None
+            kids.append((table, self.fill[par], tr))
+        for o in olds:
+            self._free_impl(o)
+        for nw, (table, fill, tr) in zip(news, kids):
+            self.tables[nw] = table
+            self.fill[nw] = fill
+            if tr is not None:
+                self.track[nw] = tr
+                if tr.tracked:
+                    self.index.on_fork(nw, tr)
+        return self.append_batch(news, 1 if news else 0,
+                                 None if tokens is None else [[t] for t in tokens])
 
     # -- prefix reuse (oracle/prefix_cache.py) -----------------------------------
     def _release_index_ref(self, b: int):

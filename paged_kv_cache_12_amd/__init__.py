@@ -51,6 +51,9 @@ SIGNATURES = {
     "pa_seq_create_cached": (_i, [_vp, _i64, _vp, _i, _vp, _i, _vp, _i, _vp, _vp]),
     "pa_seq_append_tokens": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp]),
     "pa_prefix_stats": (_i, [_vp, _vp]),
+    "pa_seq_beam_step": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp]),
+    "pa_beam_decode_step": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                                 _vp, _vp, _i, _f, _i, _i, _vp, _vp, _sz, _vp, _sz, _i, _vp]),
     "pa_decode_step_staging_size": (_sz, [_i, _i]),
     "pa_decode_step": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _f,
                             _i, _i, _vp, _vp, _sz, _vp, _sz, _i, _vp]),
@@ -297,6 +300,32 @@ def pa_decode_step(pool: "Pool", seqs: np.ndarray, k_new, v_new, k_cache, v_cach
     _check(st, "pa_decode_step")
 
 
+def pa_beam_decode_step(pool: "Pool", old_beams, parents, new_beams, k_new, v_new, k_cache,
+                        v_cache, q, out, scale: float, partition_size: int,
+                        max_blocks_per_seq: int, host_staging, dev_staging, workspace,
+                        stream=None):
+    """One beam-search iteration in one native call (pool beam step, staging copy,
+    copy-on-write, block write, decode).  Ids: int64 numpy arrays; k_new, v_new
+    [len(new_beams)][H_kv][d], q / out [len(new_beams)][H_q][d] GPU tensors."""
+    nb, H_kv, bs, d = cache_geometry(k_cache, v_cache)
+    old = np.ascontiguousarray(old_beams, dtype=np.int64)
+    par = np.ascontiguousarray(parents, dtype=np.int64)
+    new = np.ascontiguousarray(new_beams, dtype=np.int64)
+    H_q = q.shape[1]
+    if not host_staging.is_pinned():
+        raise ValueError("host_staging must be pinned host memory")
+    sbytes = min(host_staging.numel(), dev_staging.numel())
+    st = lib().pa_beam_decode_step(pool._h, _np_ptr(old), old.size, _np_ptr(par), _np_ptr(new),
+                                   new.size, _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
+                                   _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                   nb, H_kv, d, bs, _dev_ptr(q, "q"), _dev_ptr(out, "out"), H_q,
+                                   float(scale), partition_size, max_blocks_per_seq,
+                                   host_staging.data_ptr(), _dev_ptr(dev_staging, "dev_staging"),
+                                   sbytes, _dev_ptr(workspace, "workspace"), workspace.numel(),
+                                   torch_dtype_code(q), _stream_ptr(stream))
+    _check(st, "pa_beam_decode_step")
+
+
 def sha256(data: bytes) -> bytes:
     out = (ctypes.c_uint8 * 32)()
     _check(lib().pa_sha256(data, len(data), out), "pa_sha256")
@@ -410,6 +439,22 @@ class Pool:
         s = np.zeros(5, dtype=np.int64)
         _check(lib().pa_pool_stats(self._h, _np_ptr(s)), "pa_pool_stats")
         return dict(zip(("free", "used", "shared", "tokens", "copies"), s.tolist()))
+
+    def beam_step(self, old_beams, parents, new_beams, tokens=None):
+        """-> (status, slots int64 [n_new], pairs int32 [p][2])."""
+        old = np.ascontiguousarray(old_beams, dtype=np.int64)
+        par = np.ascontiguousarray(parents, dtype=np.int64)
+        new = np.ascontiguousarray(new_beams, dtype=np.int64)
+        tk = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(max(1, new.size), dtype=np.int64)
+        pairs = np.empty((max(1, new.size), 2), dtype=np.int32)
+        npairs = ctypes.c_int(0)
+        st = lib().pa_seq_beam_step(self._h, _np_ptr(old), old.size, _np_ptr(par), _np_ptr(new),
+                                    new.size, None if tk is None else _np_ptr(tk),
+                                    _np_ptr(slots), _np_ptr(pairs), ctypes.byref(npairs))
+        if st != PA_OK:
+            return st, slots[:0], pairs[:0]
+        return st, slots[:new.size], pairs[:npairs.value]
 
     # -- swapping ----------------------------------------------------------------
     def set_host_blocks(self, n: int) -> int:

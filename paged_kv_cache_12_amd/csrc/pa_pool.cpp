@@ -190,12 +190,10 @@ PA_EXPORT pa_status pa_seq_append(pa_pool* p, int64_t seq, int num_tokens, int64
   return pa_seq_append_batch(p, &seq, 1, num_tokens, slots_out, pairs_out, num_pairs_out);
 }
 
-PA_EXPORT pa_status pa_seq_free(pa_pool* p, int64_t seq) {
-  if (!p) return PA_ERR_INVALID;
-  ++p->tick;
-  auto it = p->seqs.find(seq);
-  if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
-  p->untrack(seq, it->second);
+namespace {
+
+void free_impl(pa_pool* p, std::unordered_map<int64_t, Seq>::iterator it) {
+  p->untrack(it->first, it->second);
   if (it->second.swapped) {
     for (int32_t h : it->second.table) p->host_release(h);
     --p->swapped;
@@ -204,7 +202,66 @@ PA_EXPORT pa_status pa_seq_free(pa_pool* p, int64_t seq) {
   }
   p->tokens -= it->second.fill;
   p->seqs.erase(it);
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_seq_free(pa_pool* p, int64_t seq) {
+  if (!p) return PA_ERR_INVALID;
+  ++p->tick;
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+  free_impl(p, it);
   return PA_OK;
+}
+
+PA_EXPORT pa_status pa_seq_beam_step(pa_pool* p, const int64_t* old_beams, int n_old,
+                                     const int64_t* parents, const int64_t* new_beams, int n_new,
+                                     const int32_t* tokens, int64_t* slots_out,
+                                     int32_t* pairs_out, int* num_pairs_out) {
+  if (!p || n_old < 0 || n_new < 0) return PA_ERR_INVALID;
+  if ((n_old > 0 && !old_beams) ||
+      (n_new > 0 && (!parents || !new_beams || !slots_out || !pairs_out)))
+    return PA_ERR_INVALID;
+  if (num_pairs_out) *num_pairs_out = 0;
+  std::vector<std::unordered_map<int64_t, Seq>::iterator> olds(n_old);
+  for (int i = 0; i < n_old; ++i) {
+    olds[i] = p->seqs.find(old_beams[i]);
+    if (olds[i] == p->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+  }
+  std::unordered_map<int64_t, int> is_old;
+  for (int i = 0; i < n_old; ++i) {
+    if (olds[i]->second.swapped) return PA_ERR_INVALID;
+    if (!is_old.emplace(old_beams[i], i).second) return PA_ERR_INVALID;
+  }
+  {
+    std::vector<int64_t> ids(new_beams, new_beams + n_new);
+    std::sort(ids.begin(), ids.end());
+    if (std::adjacent_find(ids.begin(), ids.end()) != ids.end()) return PA_ERR_INVALID;
+  }
+  for (int j = 0; j < n_new; ++j) {
+    if (!is_old.count(parents[j])) return PA_ERR_INVALID;
+    if (p->seqs.count(new_beams[j]) && !is_old.count(new_beams[j])) return PA_ERR_INVALID;
+  }
+  ++p->tick;
+  // 1. the new beams map their parents' blocks (before any old beam goes)
+  std::vector<Seq> kids;
+  kids.reserve(n_new);
+  for (int j = 0; j < n_new; ++j) {
+    kids.push_back(olds[is_old[parents[j]]]->second);
+    for (int32_t b : kids.back().table) p->retain(b);
+    p->tokens += kids.back().fill;
+  }
+  // 2. the old beams retire
+  for (int i = 0; i < n_old; ++i) free_impl(p, p->seqs.find(old_beams[i]));
+  // 3. the new beams take their ids
+  for (int j = 0; j < n_new; ++j) {
+    Seq& cs = p->seqs.emplace(new_beams[j], std::move(kids[j])).first->second;
+    if (cs.tracked && p->index) p->index->on_fork(*p, new_beams[j], cs);
+  }
+  // 4. one token each, copy-on-write in the order given
+  return append_batch_impl(p, new_beams, n_new, n_new > 0 ? 1 : 0, tokens, slots_out, pairs_out,
+                           num_pairs_out);
 }
 
 PA_EXPORT pa_status pa_seq_block_table(const pa_pool* p, int64_t seq, int32_t* out, int cap,

@@ -165,6 +165,23 @@ class PagedKVCache:
             pa_write_kv(k_new, v_new, self.k_cache, self.v_cache, ds, stream=stream)
         return slots, pairs
 
+    # -- beam search ----------------------------------------------------------------
+    def beam_step(self, old_beams, parents, new_beams, k_new, v_new, tokens=None, stream=None):
+        """One beam-search step: new beams fork their parents, old beams retire,
+        each new beam gets one position (k_new / v_new [len(new_beams)][H][d]);
+        the copy-on-write copies run before the block write."""
+        torch = self.torch
+        st, slots, pairs = self.pool.beam_step(old_beams, parents, new_beams, tokens)
+        if st != PA_OK:
+            raise PAError(st, "pa_seq_beam_step")
+        if len(pairs):
+            dp = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device)
+            pa_copy_blocks(self.k_cache, self.v_cache, dp, stream=stream)
+        if len(slots):
+            ds = torch.from_numpy(np.ascontiguousarray(slots)).to(self.device)
+            pa_write_kv(k_new, v_new, self.k_cache, self.v_cache, ds, stream=stream)
+        return slots, pairs
+
     # -- append: pool slots, copy-on-write, block write ----------------------
     def append(self, seqs, k: int, k_new, v_new, stream=None):
         """Append k tokens to each sequence in `seqs` (in order).  k_new, v_new:

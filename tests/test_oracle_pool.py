@@ -364,3 +364,66 @@ def test_swap_no_blocks_leaves_everything_unchanged():
                     {s: list(t) for s, t in p.tables.items()}, set(p.swapped))
     assert p.swap_in([0]) == (INVALID, [])
     assert p.swap_out([0, 9]) == (UNKNOWN_SEQ, [])
+
+
+# -- beam search (tonho.wtf "como funciona") ------------------------------------
+
+@pytest.mark.parametrize("seed", range(3))
+def test_beam_steps_keep_every_beam_content_and_share_ancestry(seed):
+    rng = random.Random(seed)
+    W, bs = 4, 4
+    p = PoolModel(200, bs, rng.sample(range(200), 200))
+    c = ContentModel(p)
+    c.new(0)
+    c.append([0], 10, rng)                   # prompt, last block partly filled
+    beams = [0]
+    nxt = 1
+    for step in range(30):
+        parents = [rng.choice(beams) for _ in range(W)]
+        news = list(range(nxt, nxt + W))
+        nxt += W
+        toks = [rng.randrange(1 << 30) for _ in news]
+        st, slots, pairs = p.beam_step(beams, parents, news)
+        assert st == OK
+        # content: children inherit the parent's tokens, copies carry them
+        for src, dst in pairs:
+            c.gpu[dst] = list(c.gpu[src])
+        for nw, par in zip(news, parents):
+            c.expect[nw] = list(c.expect[par])
+        for b in beams:
+            del c.expect[b]
+        for nw, sl, tok in zip(news, slots, toks):
+            bb, o = divmod(sl, bs)
+            c.gpu.setdefault(bb, [None] * bs)[o] = tok
+            c.expect[nw].append(tok)
+        beams = news
+        check_invariants(p)
+        c.check()
+        # one copy per extra holder of a shared, partly filled last block
+        n = p.fill[beams[0]] - 1
+        holders = {}
+        for par in parents:
+            holders[par] = holders.get(par, 0) + 1
+        expect_copies = sum(h - 1 for h in holders.values()) if n % bs else 0
+        assert len(pairs) == expect_copies
+        # beams with a common ancestor share the blocks before the divergence
+        assert p.tables[beams[0]][0] == p.tables[beams[-1]][0]
+        assert p.ref[p.tables[beams[0]][0]] == W
+
+
+def test_beam_step_checks_before_changing_anything():
+    p = PoolModel(16, 4)
+    p.create(0)
+    p.append(0, 5)
+    p.create(7)
+    snap = (list(p.free), list(p.ref), {s: list(t) for s, t in p.tables.items()})
+    assert p.beam_step([0, 9], [0], [1])[0] == UNKNOWN_SEQ
+    assert p.beam_step([0, 0], [0], [1])[0] == INVALID
+    assert p.beam_step([0], [7], [1])[0] == INVALID        # parent not an old beam
+    assert p.beam_step([0], [0, 0], [1, 1])[0] == INVALID  # repeated new id
+    assert p.beam_step([0], [0], [7])[0] == INVALID        # id of a live non-beam
+    assert snap == (list(p.free), list(p.ref), {s: list(t) for s, t in p.tables.items()})
+    st, slots, pairs = p.beam_step([0], [0, 0, 0], [0, 1, 2])   # reuse the old id
+    assert st == OK and len(slots) == 3 and len(pairs) == 2
+    assert p.beam_step([0, 1, 2], [], [])[0] == OK              # all beams retire
+    assert set(p.tables) == {7}

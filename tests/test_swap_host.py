@@ -148,3 +148,38 @@ def test_swap_is_all_or_nothing(L):
     t0, t2 = pool.block_table(0)[0].tolist(), pool.block_table(2)[0].tolist()
     assert t0 == t2 and all(pool.refcount(b) == 2 for b in t0)      # still shared
     assert pool.stats()["shared"] == 3
+
+
+@pytest.mark.parametrize("seed,bs", [(21, 4), (22, 16)])
+def test_beam_fuzz_bit_exact_against_model(L, seed, bs):
+    rng = random.Random(seed)
+    N = 301
+    order = rng.sample(range(N), N)
+    pool, model = pa.Pool(N, bs, order), PoolModel(N, bs, order)
+    groups = {}
+    nxt = 0
+    for g in range(6):
+        pool.create(nxt); model.create(nxt)
+        k = rng.randint(1, 3 * bs)
+        assert pool.append(nxt, k)[0] == model.append(nxt, k)[0] == 0
+        groups[g] = [nxt]
+        nxt += 1
+    for it in range(400):
+        g = rng.randrange(6)
+        beams = groups[g]
+        W = rng.randint(1, 5)
+        parents = [rng.choice(beams) for _ in range(W)]
+        reuse = rng.random() < 0.5
+        news = (beams + list(range(nxt, nxt + W)))[:W] if reuse else list(range(nxt, nxt + W))
+        nxt += W
+        if rng.random() < 0.05:
+            parents[0] = 10 ** 9                       # error path
+        a = pool.beam_step(beams, parents, news)
+        b = model.beam_step(beams, parents, news)
+        assert a[0] == b[0], (it, a[0], b[0])
+        assert a[1].tolist() == b[1] and [tuple(x) for x in a[2].tolist()] == b[2]
+        if a[0] == 0 or a[0] == pa.PA_ERR_NO_BLOCKS:
+            groups[g] = news
+        if it % 20 == 0:
+            compare(pool, model)
+    compare(pool, model)
