@@ -119,6 +119,32 @@ def fill_cache(sc, cache, dev):
     torch.cuda.synchronize()
 
 
+def cascade_plan(pa, torch, dev, tab_h, len_h, wl, part, flags):
+    """Shared-prefix plan for a decode over these tables (None when no group
+    of sequences shares 512 or more tokens of blocks, or blocks are not
+    shared at all)."""
+    if not flags or wl.dtype == "f32":
+        return None
+    pre, groups, members, mp = pa.pa_cascade_plan(tab_h, len_h, wl.block_size, wl.h_q, wl.h_kv,
+                                                  512)
+    if len(groups) == 0:
+        return None
+    put = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return {"prefix": put(pre), "groups": put(groups.reshape(-1)), "members": put(members),
+            "max_prefix": mp, "ngroups": len(groups)}
+
+
+def run_decode(pa, out, q, cache, d_tab, d_len, max_ctx, wl, part, ws, flags, order, plan):
+    kc, vc = cache if isinstance(cache, tuple) else (cache.k_cache, cache.v_cache)
+    if plan is None:
+        pa.pa_decode(out, q, kc, vc, d_tab, d_len, max_ctx, wl.scale, part, workspace=ws,
+                     flags=flags, seq_order=order)
+    else:
+        pa.pa_decode_cascade(out, q, kc, vc, d_tab, d_len, max_ctx, wl.scale, part,
+                             plan["prefix"], plan["groups"], plan["members"], plan["max_prefix"],
+                             ws, flags=flags, seq_order=order)
+
+
 def unique_kv_bytes(tables, lens, wl):
     """KV bytes of the distinct physical blocks the batch reads (a block
     aliased by several sequences counts once, with its filled positions)."""
@@ -530,7 +556,8 @@ def main():
     maxb = -(-max_ctx_end // wl.block_size)
     q = storage_to_torch(sc.q, wl.dtype).to(dev)
     out = torch.empty_like(q)
-    ws_bytes = pa.pa_decode_workspace_size(B, wl.h_q, wl.head_dim, max_ctx_end, part)
+    ws_bytes = max(pa.pa_decode_workspace_size(B, wl.h_q, wl.head_dim, max_ctx_end, part),
+                   pa.pa_decode_cascade_workspace_size(B, wl.h_q, wl.head_dim, max_ctx_end, part))
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     step_bytes = []
@@ -568,11 +595,12 @@ def main():
         max_ctx0 = int(len_h.max())
         kv0 = float(len_h.sum()) * 2 * wl.h_kv * wl.head_dim * e
         order0 = torch.from_numpy(pa.pa_decode_order(tab_h, len_h)).to(dev)
+        plan0 = cascade_plan(pa, torch, dev, tab_h, len_h, wl, part, flags)
 
         def step(i):
             h0 = time.perf_counter()
-            pa.pa_decode(out, q, cache.k_cache, cache.v_cache, d_tab, d_len, max_ctx0,
-                         wl.scale, part, workspace=ws, flags=flags, seq_order=order0)
+            run_decode(pa, out, q, cache, d_tab, d_len, max_ctx0, wl, part, ws, flags, order0,
+                       plan0)
             host_s.append(time.perf_counter() - h0)
             step_bytes.append(kv0)
 
@@ -612,10 +640,12 @@ def main():
     copies = [(cache.k_cache, cache.v_cache)] + [
         (cache.k_cache.clone(), cache.v_cache.clone()) for _ in range(nrot - 1)]
 
+    plan = cascade_plan(pa, torch, dev, tab_h, len_h, wl, part, flags)
+
     def decode(i):
         kc, vc = copies[i % nrot]
-        pa.pa_decode(out, q, kc, vc, d_tab, d_len, max_ctx, wl.scale, part,
-                     workspace=ws, flags=flags, seq_order=d_order)
+        run_decode(pa, out, q, (kc, vc), d_tab, d_len, max_ctx, wl, part, ws, flags, d_order,
+                   plan)
 
     def bracketed(n, rotate):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -708,8 +738,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(unique_rate, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(unique_rate / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "pa_decode" + (" (partition kernel + reduce)"
-                                              if ws_bytes else " (one kernel)"),
+                     "kernel": "pa_decode" + (" (shared-prefix pass + rest + reduce)"
+                                              if plan is not None else
+                                              " (partition kernel + reduce)"
+                                              if pa.pa_decode_workspace_size(
+                                                  B, wl.h_q, wl.head_dim, max_ctx_end, part)
+                                              else " (one kernel)"),
+                     "cascade_groups": 0 if plan is None else plan["ngroups"],
                      "bytes_per_launch": round(unique),
                      "logical_bytes_per_launch": round(kv_dec),
                      "logical_achieved": round(achieved, 1)},

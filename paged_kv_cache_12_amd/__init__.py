@@ -39,6 +39,10 @@ SIGNATURES = {
     "pa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                        _i, _vp, _sz, _i, _i, _vp]),
     "pa_decode_order": (_i, [_vp, _i, _vp, _i, _vp]),
+    "pa_cascade_plan": (_i, [_vp, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "pa_decode_cascade_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "pa_decode_cascade": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                               _f, _i, _vp, _vp, _vp, _i, _i, _vp, _sz, _i, _i, _vp]),
     "pa_swap_blocks": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _vp]),
     "pa_pool_set_host_blocks": (_i, [_vp, _i]),
     "pa_seq_swap_out": (_i, [_vp, _vp, _i, _vp, _i, _vp]),
@@ -273,6 +277,57 @@ def pa_decode_order(block_tables: np.ndarray, context_lens: np.ndarray) -> np.nd
     _check(lib().pa_decode_order(_np_ptr(tab), tab.shape[1], _np_ptr(lens), B, _np_ptr(out)),
            "pa_decode_order")
     return out
+
+
+def pa_cascade_plan(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
+                    num_q_heads: int, num_kv_heads: int, min_prefix: int = 512):
+    """Host plan of the shared-prefix pass: (prefix_len int32 [B], groups int32
+    [n][3], members int32 [m], max_prefix)."""
+    tab = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B = lens.size
+    if tab.ndim != 2 or tab.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    pre = np.zeros(max(1, B), dtype=np.int32)
+    groups = np.zeros((max(1, B), 3), dtype=np.int32)
+    members = np.zeros(max(1, B), dtype=np.int32)
+    ng, mp = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().pa_cascade_plan(_np_ptr(tab), tab.shape[1], _np_ptr(lens), B, block_size,
+                                 num_q_heads, num_kv_heads, min_prefix, _np_ptr(pre),
+                                 _np_ptr(groups), _np_ptr(members), ctypes.byref(ng),
+                                 ctypes.byref(mp)), "pa_cascade_plan")
+    g = groups[:ng.value]
+    nm = int(g[:, 1].sum()) if ng.value else 0
+    return pre[:B], g, members[:nm], mp.value
+
+
+def pa_decode_cascade_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int,
+                                     max_context_len: int, partition_size: int) -> int:
+    return int(lib().pa_decode_cascade_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                      max_context_len, partition_size))
+
+
+def pa_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                      scale: float, partition_size: int, prefix_len, groups, members,
+                      max_prefix: int, workspace, stream=None, flags: int = 0, seq_order=None):
+    """pa_decode with a shared-prefix plan (GPU int32 tensors from pa_cascade_plan)."""
+    torch = _torch()
+    nb, H_kv, bs, d = cache_geometry(k_cache, v_cache)
+    B, H_q, _ = q.shape
+    ng = groups.numel() // 3
+    for t, name in ((prefix_len, "prefix_len"), (groups, "groups"), (members, "members")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    st = lib().pa_decode_cascade(
+        _dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
+        _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables"),
+        block_tables.shape[1], _dev_ptr(context_lens, "context_lens"),
+        None if seq_order is None else _dev_ptr(seq_order, "seq_order"), B, max_context_len, H_q,
+        H_kv, d, bs, nb, float(scale), partition_size, _dev_ptr(prefix_len, "prefix_len"),
+        _dev_ptr(groups, "groups"), _dev_ptr(members, "members"), ng, max_prefix,
+        _dev_ptr(workspace, "workspace"), workspace.numel(), torch_dtype_code(q), flags,
+        _stream_ptr(stream))
+    _check(st, "pa_decode_cascade")
 
 
 def pa_decode_step_staging_size(num_seqs: int, max_blocks_per_seq: int) -> int:

@@ -92,27 +92,26 @@ struct ChunkSpan {
   int nchunks, t0, t1;
 };
 
-// Token range of wave `wave` in chunk `ch` of sequence s: partition
-// ch * NW + wave of `part` tokens, or with part == 0 an even split of the whole
-// context into NW runs of whole 32-token groups.
+// Chunks covering n tokens (at least one, also for n == 0).
 template <int NW>
-__device__ __forceinline__ ChunkSpan chunk_span(const int32_t* ctx_lens, int s, int max_tokens,
-                                                int part, int ch, int wave) {
+__device__ __forceinline__ int chunks_of(int n, int part) {
+  if (part <= 0) return 1;
+  const int nparts = (n + part - 1) / part;
+  return nparts > NW ? (nparts + NW - 1) / NW : 1;
+}
+
+// Token range of wave `wave` in chunk `ch` over tokens [lo, hi): partition
+// ch * NW + wave of `part` tokens, or with part == 0 an even split of the
+// range into NW runs of whole 32-token groups.
+template <int NW>
+__device__ __forceinline__ ChunkSpan range_span(int lo, int hi, int part, int ch, int wave) {
   ChunkSpan sp;
-  int ctx = ctx_lens[s];
-  ctx = ctx < 0 ? 0 : (ctx > max_tokens ? max_tokens : ctx);
-  int unit;
-  if (part > 0) {
-    const int nparts = (ctx + part - 1) / part;
-    sp.nchunks = nparts > NW ? (nparts + NW - 1) / NW : 1;
-    unit = part;
-  } else {
-    sp.nchunks = 1;
-    unit = (((ctx + NW - 1) / NW) + 31) & ~31;
-  }
-  const int64_t lo = (static_cast<int64_t>(ch) * NW + wave) * unit;
-  sp.t0 = lo < ctx ? static_cast<int>(lo) : ctx;
-  sp.t1 = lo + unit < ctx ? static_cast<int>(lo + unit) : ctx;
+  const int n = hi > lo ? hi - lo : 0;
+  sp.nchunks = chunks_of<NW>(n, part);
+  const int unit = part > 0 ? part : (((n + NW - 1) / NW) + 31) & ~31;
+  const int64_t a = (static_cast<int64_t>(ch) * NW + wave) * unit;
+  sp.t0 = lo + (a < n ? static_cast<int>(a) : n);
+  sp.t1 = lo + (a + unit < n ? static_cast<int>(a + unit) : n);
   return sp;
 }
 
@@ -309,14 +308,34 @@ __device__ __forceinline__ void compute_group(GroupTiles<T, D>& G,
 // the middle of the KV read stream are expensive on this part (a few KiB per
 // work unit cost up to ~18 % of bandwidth), hence one write per NW partitions.
 // With part == 0 the context is one chunk split evenly across the waves.
-template <typename T, int D, int BS, int NW, bool NT>
+// Work decomposition of decode_part_mfma:
+//   kPlain   one work-group per (chunk, KV head [x head group], sequence);
+//   kSuffix  the same over tokens [prefix_len[s], ctx) of each sequence, always
+//            writing partials after the sequence's prefix-pass partials when
+//            prefix_len[s] > 0;
+//   kPrefix  one work-group per (chunk, KV head, column group): the sequences
+//            of a group share the physical blocks of their first L tokens, and
+//            their queries fill the 16 MFMA columns (member c / G, head c % G),
+//            so each K/V load serves all of them; partials only.
+enum { kPlain = 0, kSuffix = 1, kPrefix = 2 };
+
+// Cascade description on the device: prefix_len[B]; groups[ng][3] =
+// {first member, member count, L}; members[] = sequence indices.
+struct Cascade {
+  const int32_t* prefix_len;
+  const int32_t* groups;
+  const int32_t* members;
+  int ngroups;
+};
+
+template <typename T, int D, int BS, int NW, bool NT, int MODE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PA_WAVES)))
 void decode_part_mfma(
     T* __restrict__ out, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ block_tables, int maxb, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ order, int B, int max_tokens, int H_q, int H_kv, int G,
-    int n_hg, int num_blocks, float scale_log2, int part, int maxC) {
+    int n_hg, int num_blocks, float scale_log2, int part, int maxC, int ws_stride, Cascade cas) {
   typedef Mfma<T> M;
   typedef typename M::v8 v8;
   constexpr int NC = D / 32;    // QK k-chunks of 32 dims
@@ -327,27 +346,55 @@ void decode_part_mfma(
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;  // MFMA row/column index within a lane group
   const int g = lane >> 4;  // lane group
-  const WorkItem wi = work_item<!NT>(blockIdx.x, H_kv * n_hg, B, maxC);
+  const WorkItem wi =
+      work_item<!NT>(blockIdx.x, H_kv * n_hg, MODE == kPrefix ? cas.ngroups : B, maxC);
   const int ch = wi.chunk;
   const int kvh = wi.hgl / n_hg;
   const int hg = wi.hgl - kvh * n_hg;
-  const int s = order ? order[wi.seq] : wi.seq;
-  if (s < 0 || s >= B) return;
 
-  const ChunkSpan sp = chunk_span<NW>(ctx_lens, s, max_tokens, part, ch, wave);
+  // the sequence whose table is read, this column's sequence and head, and
+  // the partial slot of chunk 0
+  int s, s_col, slot0 = 0, lo = 0, hi;
+  bool hvalid;
+  int hin;
+  if constexpr (MODE == kPrefix) {
+    const int gi = wi.seq;
+    const int first = cas.groups[3 * gi], count = cas.groups[3 * gi + 1];
+    hi = cas.groups[3 * gi + 2];
+    s = cas.members[first];
+    const int mi = c / G;
+    hin = c - mi * G;
+    hvalid = mi < count;
+    s_col = hvalid ? cas.members[first + mi] : s;
+  } else {
+    s = order ? order[wi.seq] : wi.seq;
+    if (s < 0 || s >= B) return;
+    int ctx = ctx_lens[s];
+    hi = ctx < 0 ? 0 : (ctx > max_tokens ? max_tokens : ctx);
+    if constexpr (MODE == kSuffix) {
+      lo = cas.prefix_len[s];
+      lo = lo < 0 ? 0 : (lo > hi ? hi : lo);
+      if (lo > 0) slot0 = chunks_of<NW>(lo, part);
+    }
+    hin = hg * 16 + c;  // head within the GQA group
+    hvalid = hin < G;
+    s_col = s;
+  }
+  const ChunkSpan sp = range_span<NW>(lo, hi, part, ch, wave);
   if (ch >= sp.nchunks) return;  // uniform over the work-group
   const int t0 = sp.t0, t1 = sp.t1;
-
-  const int hin = hg * 16 + c;  // head within the GQA group
-  const bool hvalid = hin < G;
   const int qh = kvh * G + hin;
+  // the final output is written here only for a context in one chunk with no
+  // prefix pass
+  const bool final_out = MODE == kPlain ? sp.nchunks == 1
+                                        : (MODE == kSuffix && slot0 == 0 && sp.nchunks == 1);
 
   // B operand of QK: Q[head c][dims 8(4k+g) .. +8] for chunk k.
   v8 qop[NC];
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     if (hvalid)
-      qop[k] = *reinterpret_cast<const v8*>(q + (static_cast<int64_t>(s) * H_q + qh) * D +
+      qop[k] = *reinterpret_cast<const v8*>(q + (static_cast<int64_t>(s_col) * H_q + qh) * D +
                                             (4 * k + g) * 8);
     else
       qop[k] = v8{};
@@ -440,8 +487,8 @@ void decode_part_mfma(
   }
 
   if (!hvalid) return;
-  const int64_t row = static_cast<int64_t>(s) * H_q + qh;
-  if (sp.nchunks == 1) {
+  const int64_t row = static_cast<int64_t>(s_col) * H_q + qh;
+  if (final_out) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     T* dst = out + row * D + 4 * g;
 #pragma unroll
@@ -449,10 +496,11 @@ void decode_part_mfma(
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[16 * j + r] = static_cast<T>(o[j][r] * inv);
   } else {
-    float* dst = ws_o + (row * maxC + ch) * D + 4 * g;
+    const int64_t slot = row * ws_stride + slot0 + ch;
+    float* dst = ws_o + slot * D + 4 * g;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = o[j];
-    if (g == 0) ws_ml[row * maxC + ch] = make_float2(m, lt);
+    if (g == 0) ws_ml[slot] = make_float2(m, lt);
   }
 }
 
@@ -580,11 +628,11 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return r;
 }
 
-template <typename T, int D>
+template <typename T, int D, int NW>
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce(
     T* __restrict__ out, const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
     const int32_t* __restrict__ ctx_lens, int max_tokens, int H_q, int part, int maxP,
-    int per_chunk) {
+    const int32_t* __restrict__ prefix_len) {
   constexpr int TPR = D / 4;                  // threads per partition row
   constexpr int PL = kReduceThreads / TPR;    // partition lanes
   __shared__ float sh_w[kReduceChunk];
@@ -593,10 +641,18 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce(
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int tid = threadIdx.x;
-  // partials: one per chunk of per_chunk partitions of the sequence
-  const Span sp = partition_span(ctx_lens, s, max_tokens, part, 0);
-  const int nchunks = (sp.nparts + per_chunk - 1) / per_chunk;
-  if (nchunks <= 1) return;
+  // partials: one per chunk of the sequence's context, or, with a prefix
+  // pass, one per chunk of the prefix and then one per chunk of the rest
+  int ctx = ctx_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > max_tokens ? max_tokens : ctx);
+  int nchunks;
+  if (prefix_len && prefix_len[s] > 0) {
+    const int L = prefix_len[s] < ctx ? prefix_len[s] : ctx;
+    nchunks = chunks_of<NW>(L, part) + chunks_of<NW>(ctx - L, part);
+  } else {
+    nchunks = chunks_of<NW>(ctx, part);
+    if (nchunks <= 1) return;
+  }
   const int np = nchunks < maxP ? nchunks : maxP;
   const int64_t row = static_cast<int64_t>(s) * H_q + h;
   const float2* ml = ws_ml + row * maxP;
@@ -671,31 +727,56 @@ struct DecodeArgs {
   float* ws_o;
   float2* ws_ml;
   hipStream_t st;
+  Cascade cas;           // ngroups > 0: prefix pass + suffix pass
+  int max_prefix;        // longest group prefix
 };
 
-template <typename T, int D, int BS, int NW, bool NT>
-void launch_part(const DecodeArgs& a, int maxC) {
+template <typename T, int D, int BS, int NW, bool NT, int MODE>
+void launch_part(const DecodeArgs& a, int maxC, int ws_stride, int nitems) {
   const int n_hg = (a.G + 15) / 16;
-  const int64_t grid = static_cast<int64_t>(maxC) * a.H_kv * n_hg * a.B;
-  hipLaunchKernelGGL((decode_part_mfma<T, D, BS, NW, NT>), dim3(static_cast<unsigned>(grid)),
-                     dim3(64 * NW), 0, a.st, static_cast<T*>(a.out), a.ws_o, a.ws_ml,
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.kc),
-                     static_cast<const T*>(a.vc), a.bt, a.maxb, a.lens, a.order, a.B,
-                     a.max_tokens, a.H_q, a.H_kv, a.G, n_hg, a.num_blocks, a.scale_log2, a.part,
-                     maxC);
+  const int64_t grid = static_cast<int64_t>(maxC) * a.H_kv * n_hg * nitems;
+  if (grid == 0) return;
+  hipLaunchKernelGGL((decode_part_mfma<T, D, BS, NW, NT, MODE>),
+                     dim3(static_cast<unsigned>(grid)), dim3(64 * NW), 0, a.st,
+                     static_cast<T*>(a.out), a.ws_o, a.ws_ml, static_cast<const T*>(a.q),
+                     static_cast<const T*>(a.kc), static_cast<const T*>(a.vc), a.bt, a.maxb,
+                     a.lens, a.order, a.B, a.max_tokens, a.H_q, a.H_kv, a.G, n_hg, a.num_blocks,
+                     a.scale_log2, a.part, maxC, ws_stride, a.cas);
+}
+
+// Partial slots per (sequence, query head) row.
+inline int host_chunks(int n, int part, int nw) {
+  if (part <= 0) return 1;
+  const int nparts = (n + part - 1) / part;
+  return nparts > nw ? (nparts + nw - 1) / nw : 1;
 }
 
 template <typename T, int D, int BS, int NW>
 void launch_mfma_nw(const DecodeArgs& a) {
   const int maxC = num_chunks(a.maxP, NW);
+  if (a.cas.ngroups == 0) {
+    if (a.shared_kv)
+      launch_part<T, D, BS, NW, false, kPlain>(a, maxC, maxC, a.B);
+    else
+      launch_part<T, D, BS, NW, true, kPlain>(a, maxC, maxC, a.B);
+    if (maxC > 1)
+      hipLaunchKernelGGL((decode_reduce<T, D, NW>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0,
+                         a.st, static_cast<T*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens,
+                         a.H_q, a.part, maxC, nullptr);
+    return;
+  }
+  // prefix pass (groups re-read the same blocks: cached loads), then the rest
+  // of every sequence, then the merge; row stride maxC + 1 slots
+  const int stride = maxC + 1;
+  launch_part<T, D, BS, NW, false, kPrefix>(a, host_chunks(a.max_prefix, a.part, NW), stride,
+                                            a.cas.ngroups);
   if (a.shared_kv)
-    launch_part<T, D, BS, NW, false>(a, maxC);
+    launch_part<T, D, BS, NW, false, kSuffix>(a, maxC, stride, a.B);
   else
-    launch_part<T, D, BS, NW, true>(a, maxC);
-  if (maxC > 1)
-    hipLaunchKernelGGL((decode_reduce<T, D>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0, a.st,
-                       static_cast<T*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens, a.H_q,
-                       a.part, maxC, NW);
+    launch_part<T, D, BS, NW, true, kSuffix>(a, maxC, stride, a.B);
+  hipLaunchKernelGGL((decode_reduce<T, D, NW>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0, a.st,
+                     static_cast<T*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens, a.H_q,
+                     a.part, stride, a.cas.prefix_len);
 }
 
 // Waves per work-group for a partition size (see kChunkTokens).
@@ -723,9 +804,9 @@ void launch_f32(const DecodeArgs& a) {
                      a.maxb, a.lens, a.max_tokens, a.H_q, a.H_kv, a.G, a.num_blocks,
                      a.scale_log2, a.part, a.maxP);
   if (a.maxP > 1)
-    hipLaunchKernelGGL((decode_reduce<float, D>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0, a.st,
-                       static_cast<float*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens, a.H_q,
-                       a.part, a.maxP, 1);
+    hipLaunchKernelGGL((decode_reduce<float, D, 1>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0,
+                       a.st, static_cast<float*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens,
+                       a.H_q, a.part, a.maxP, nullptr);
 }
 
 template <typename T>
@@ -740,6 +821,20 @@ void dispatch_mfma(const DecodeArgs& a, int D, int BS) {
 }  // namespace pa
 
 using namespace pa;
+
+PA_EXPORT size_t pa_decode_cascade_workspace_size(int num_seqs, int num_q_heads, int head_dim,
+                                                  int max_context_len, int partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+      partition_size < 0)
+    return 0;
+  const int maxP = num_partitions(max_context_len, partition_size);
+  const int part = maxP > 1 ? partition_size : 0;
+  int nw = waves_per_group(part);
+  const int stride = host_chunks(max_context_len, part, nw) + 1;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * stride;
+  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  return o_bytes + rows * sizeof(float2);
+}
 
 PA_EXPORT size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
                                           int max_context_len, int partition_size) {
@@ -761,7 +856,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                       int num_blocks, float scale, int partition_size, void* workspace,
                       size_t workspace_bytes, int dtype, int flags, const int32_t* order,
-                      void* stream) {
+                      void* stream, const CascadePlan* plan) {
   if (elem_bytes(dtype) == 0) return PA_ERR_UNSUPPORTED;
   if (flags & ~PA_DECODE_SHARED_KV) return PA_ERR_INVALID;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
@@ -781,8 +876,17 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_ERR_INVALID;
   if (num_seqs > 65535 || num_q_heads > 65535) return PA_ERR_INVALID;
-  const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
-                                               partition_size);
+  // the cascade runs on the fp16 / bf16 path for up to 16 query heads per KV head
+  const bool cascade = plan && plan->ngroups > 0 && dtype != PA_F32 &&
+                       num_q_heads / num_kv_heads <= 16;
+  if (cascade && (!plan->prefix_len || !plan->groups || !plan->members || plan->ngroups < 0 ||
+                  plan->max_prefix < 0 || plan->max_prefix > max_context_len))
+    return PA_ERR_INVALID;
+  const size_t need =
+      cascade ? pa_decode_cascade_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                 max_context_len, partition_size)
+              : pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                         partition_size);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PA_ERR_INVALID;
 
@@ -805,8 +909,16 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   a.maxP = num_partitions(max_context_len, partition_size);
   a.part = a.maxP > 1 ? partition_size : 0;
+  a.cas = Cascade{nullptr, nullptr, nullptr, 0};
+  a.max_prefix = 0;
+  size_t slots = a.maxP;
+  if (cascade) {
+    a.cas = Cascade{plan->prefix_len, plan->groups, plan->members, plan->ngroups};
+    a.max_prefix = plan->max_prefix;
+    slots = host_chunks(max_context_len, a.part, waves_per_group(a.part)) + 1;
+  }
   if (need > 0) {
-    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * a.maxP;
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * slots;
     const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     a.ws_o = static_cast<float*>(workspace);
     a.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + o_bytes);
@@ -841,5 +953,24 @@ PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* k_cache, con
   return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, flags,
-                     seq_order, stream);
+                     seq_order, stream, nullptr);
+}
+
+PA_EXPORT pa_status pa_decode_cascade(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      int max_blocks_per_seq, const int32_t* context_lens,
+                                      const int32_t* seq_order, int num_seqs, int max_context_len,
+                                      int num_q_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int num_blocks, float scale,
+                                      int partition_size, const int32_t* prefix_len,
+                                      const int32_t* groups, const int32_t* members,
+                                      int num_groups, int max_prefix, void* workspace,
+                                      size_t workspace_bytes, int dtype, int flags,
+                                      void* stream) {
+  if (num_groups < 0) return PA_ERR_INVALID;
+  const CascadePlan plan{prefix_len, groups, members, num_groups, max_prefix};
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, flags,
+                     seq_order, stream, &plan);
 }

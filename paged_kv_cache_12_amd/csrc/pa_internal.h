@@ -33,14 +33,26 @@ inline pa_status launch_status() {
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+// Shared-prefix (cascade) plan, device arrays: prefix_len[num_seqs],
+// groups[ngroups][3] = {first member, member count, prefix tokens},
+// members[] = sequence indices; max_prefix = largest prefix (host value).
+struct CascadePlan {
+  const int32_t* prefix_len;
+  const int32_t* groups;
+  const int32_t* members;
+  int ngroups;
+  int max_prefix;
+};
+
 // pa_decode with an optional sequence order (a permutation of 0..num_seqs-1,
-// device memory): work-groups are issued in that order.
+// device memory; work-groups are issued in that order) and an optional
+// cascade plan.
 pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, int max_blocks_per_seq,
                       const int32_t* context_lens, int num_seqs, int max_context_len,
                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                       int num_blocks, float scale, int partition_size, void* workspace,
                       size_t workspace_bytes, int dtype, int flags, const int32_t* order,
-                      void* stream);
+                      void* stream, const CascadePlan* plan);
 
 }  // namespace pa

@@ -506,6 +506,69 @@ PA_EXPORT pa_status pa_decode_order(const int32_t* block_tables, int max_blocks_
   return PA_OK;
 }
 
+PA_EXPORT pa_status pa_cascade_plan(const int32_t* block_tables, int max_blocks_per_seq,
+                                    const int32_t* context_lens, int num_seqs, int block_size,
+                                    int num_q_heads, int num_kv_heads, int min_prefix,
+                                    int32_t* prefix_len_out, int32_t* groups_out,
+                                    int32_t* members_out, int* num_groups_out,
+                                    int* max_prefix_out) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || block_size <= 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || !num_groups_out || !max_prefix_out)
+    return PA_ERR_INVALID;
+  *num_groups_out = 0;
+  *max_prefix_out = 0;
+  if (num_seqs == 0) return PA_OK;
+  if (!block_tables || !context_lens || !prefix_len_out || !groups_out || !members_out)
+    return PA_ERR_INVALID;
+  for (int s = 0; s < num_seqs; ++s) prefix_len_out[s] = 0;
+  const int G = num_q_heads / num_kv_heads;
+  const int cap = G <= 16 ? 16 / G : 0;  // sequences per 16 MFMA columns
+  if (cap < 2 || max_blocks_per_seq == 0) return PA_OK;
+  // families: sequences whose tables start with the same physical block, in
+  // order of first appearance, members in index order
+  std::unordered_map<int32_t, int32_t> fam_of;
+  std::vector<std::vector<int32_t>> fams;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int32_t b0 = block_tables[static_cast<size_t>(s) * max_blocks_per_seq];
+    if (context_lens[s] <= 0 || b0 < 0) continue;
+    auto it = fam_of.emplace(b0, static_cast<int32_t>(fams.size()));
+    if (it.second) fams.emplace_back();
+    fams[it.first->second].push_back(s);
+  }
+  int ng = 0, nm = 0;
+  for (const auto& f : fams) {
+    if (f.size() < 2) continue;
+    int min_len = context_lens[f[0]];
+    for (int32_t s : f) min_len = std::min(min_len, context_lens[s]);
+    const int nb = std::min((min_len + block_size - 1) / block_size, max_blocks_per_seq);
+    const int32_t* t0 = block_tables + static_cast<size_t>(f[0]) * max_blocks_per_seq;
+    int common = 0;
+    for (; common < nb; ++common) {
+      bool same = true;
+      for (size_t i = 1; i < f.size() && same; ++i)
+        same = block_tables[static_cast<size_t>(f[i]) * max_blocks_per_seq + common] ==
+               t0[common];
+      if (!same) break;
+    }
+    int L = std::min(common * block_size, min_len) & ~31;
+    if (L < std::max(min_prefix, 32)) continue;
+    for (size_t i = 0; i < f.size(); i += cap) {
+      const int cnt = static_cast<int>(std::min(f.size() - i, static_cast<size_t>(cap)));
+      groups_out[3 * ng] = nm;
+      groups_out[3 * ng + 1] = cnt;
+      groups_out[3 * ng + 2] = L;
+      for (int k = 0; k < cnt; ++k) {
+        members_out[nm++] = f[i + k];
+        prefix_len_out[f[i + k]] = L;
+      }
+      ++ng;
+    }
+    *max_prefix_out = std::max(*max_prefix_out, L);
+  }
+  *num_groups_out = ng;
+  return PA_OK;
+}
+
 PA_EXPORT size_t pa_kv_bytes_per_token(int num_layers, int num_kv_heads, int head_dim,
                                        int dtype) {
   size_t e;

@@ -21,7 +21,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct StagingLayout {
-  size_t slots, pairs, lens, order, tables, total;
+  size_t slots, pairs, lens, order, prefix, groups, members, tables, total;
 };
 
 StagingLayout staging_layout(int n, int maxb) {
@@ -30,10 +30,16 @@ StagingLayout staging_layout(int n, int maxb) {
   L.pairs = L.slots + align_up(sizeof(int64_t) * n);
   L.lens = L.pairs + align_up(sizeof(int32_t) * 2 * n);
   L.order = L.lens + align_up(sizeof(int32_t) * n);
-  L.tables = L.order + align_up(sizeof(int32_t) * n);
+  L.prefix = L.order + align_up(sizeof(int32_t) * n);
+  L.groups = L.prefix + align_up(sizeof(int32_t) * n);
+  L.members = L.groups + align_up(sizeof(int32_t) * 3 * n);
+  L.tables = L.members + align_up(sizeof(int32_t) * n);
   L.total = L.tables + align_up(sizeof(int32_t) * static_cast<size_t>(n) * maxb);
   return L;
 }
+
+// Shared prefixes shorter than this stay on the plain path.
+constexpr int kCascadeMinPrefix = 512;
 
 // Copies the pinned host staging buffer into device memory from a kernel on
 // the caller's stream: the compute queue does not wait on a copy engine.
@@ -132,6 +138,23 @@ pa_status launch_step(pa_pool* pool, const StepDev& a, const int64_t* seqs, int 
   st = pa_decode_order(h_tab, a.max_blocks_per_seq, h_lens, n, h_order);
   if (st != PA_OK) return st;
   const int flags = pa_pool_shared_blocks(pool) > 0 ? PA_DECODE_SHARED_KV : 0;
+  // shared prefixes: one prefix pass per group of sequences sharing blocks,
+  // when the workspace has room for the cascade's partials
+  CascadePlan plan{reinterpret_cast<const int32_t*>(d + L.prefix),
+                   reinterpret_cast<const int32_t*>(d + L.groups),
+                   reinterpret_cast<const int32_t*>(d + L.members), 0, 0};
+  if (flags && a.dtype != PA_F32 &&
+      pa_decode_cascade_workspace_size(n, a.num_q_heads, a.head_dim, max_ctx,
+                                       a.partition_size) <= a.workspace_bytes &&
+      a.workspace) {
+    st = pa_cascade_plan(h_tab, a.max_blocks_per_seq, h_lens, n, a.block_size, a.num_q_heads,
+                         a.num_kv_heads, kCascadeMinPrefix,
+                         reinterpret_cast<int32_t*>(h + L.prefix),
+                         reinterpret_cast<int32_t*>(h + L.groups),
+                         reinterpret_cast<int32_t*>(h + L.members), &plan.ngroups,
+                         &plan.max_prefix);
+    if (st != PA_OK) return st;
+  }
 
   // one host-to-device copy of slots, pairs, lengths, order and tables: a
   // copy kernel reading the pinned buffer when it is mapped on the device,
@@ -163,7 +186,7 @@ pa_status launch_step(pa_pool* pool, const StepDev& a, const int64_t* seqs, int 
                      reinterpret_cast<const int32_t*>(d + L.lens), n, max_ctx, a.num_q_heads,
                      a.num_kv_heads, a.head_dim, a.block_size, a.num_blocks, a.scale,
                      a.partition_size, a.workspace, a.workspace_bytes, a.dtype, flags,
-                     reinterpret_cast<const int32_t*>(d + L.order), a.stream);
+                     reinterpret_cast<const int32_t*>(d + L.order), a.stream, &plan);
 }
 
 }  // namespace

@@ -33,7 +33,7 @@ def L():
 
 def test_library_exports_exactly_the_header_functions(L):
     declared = header_functions()
-    assert len(declared) == 36
+    assert len(declared) == 39
     for name in declared:
         assert hasattr(L, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
@@ -268,7 +268,8 @@ def test_decode_step_rejects_before_touching_the_pool(L):
     full.append(0, 32)
     assert _step(L, full, [0]) == pa.PA_ERR_NO_BLOCKS
     assert (pool.free_list().tolist(), pool.stats()) == before
-    assert pa.pa_decode_step_staging_size(64, 257) == 512 + 512 + 256 + 256 + (64 * 257 * 4 + 255) // 256 * 256
+    # slots, pairs, lengths, order, prefix lengths, groups, members, tables
+    assert pa.pa_decode_step_staging_size(64, 257) == 512 + 512 + 256 + 256 + 256 + 768 + 256 + (64 * 257 * 4 + 255) // 256 * 256
 
 
 def _order_by_definition(tab, lens):
@@ -315,3 +316,69 @@ def test_decode_order_without_sharing_is_longest_first(L):
     assert pa.pa_decode_order(np.zeros((0, 1), np.int32), np.zeros(0, np.int32)).size == 0
     assert L.pa_decode_order(None, 1, None, 2, None) == pa.PA_ERR_INVALID
     assert L.pa_decode_order(None, 1, None, -1, None) == pa.PA_ERR_INVALID
+
+
+def _plan_by_definition(tab, lens, bs, G, min_prefix):
+    """The documented plan, written out."""
+    B = len(lens)
+    pre = [0] * B
+    groups, members = [], []
+    cap = 16 // G if G <= 16 else 0
+    if cap < 2:
+        return pre, groups, members, 0
+    fams, order = {}, []
+    for s in range(B):
+        if lens[s] <= 0 or tab[s][0] < 0:
+            continue
+        if tab[s][0] not in fams:
+            fams[tab[s][0]] = []
+            order.append(tab[s][0])
+        fams[tab[s][0]].append(s)
+    mp = 0
+    for key in order:
+        f = fams[key]
+        if len(f) < 2:
+            continue
+        mn = min(lens[s] for s in f)
+        nb = min(-(-mn // bs), tab.shape[1])
+        common = 0
+        while common < nb and all(tab[s][common] == tab[f[0]][common] for s in f):
+            common += 1
+        L = (min(common * bs, mn) // 32) * 32
+        if L < max(min_prefix, 32):
+            continue
+        for i in range(0, len(f), cap):
+            part = f[i:i + cap]
+            groups.append([len(members), len(part), L])
+            members += part
+            for s in part:
+                pre[s] = L
+        mp = max(mp, L)
+    return pre, groups, members, mp
+
+
+@pytest.mark.parametrize("seed,G", [(0, 4), (1, 1), (2, 8), (3, 16), (4, 2)])
+def test_cascade_plan_matches_its_definition(L, seed, G):
+    rng = np.random.default_rng(seed)
+    B, maxb, bs = 40, 12, 16
+    tab = np.full((B, maxb), -1, np.int32)
+    lens = rng.integers(0, maxb * bs + 1, B).astype(np.int32)
+    prefixes = [rng.integers(0, 10000, maxb) for _ in range(4)]
+    for s in range(B):
+        nb = -(-int(lens[s]) // bs)
+        fam = prefixes[s % 4]
+        keep = rng.integers(0, maxb + 1)
+        row = [int(fam[i]) if i < keep else int(rng.integers(20000, 30000)) for i in range(nb)]
+        tab[s, :nb] = row
+    for mp_min in (0, 64, 512):
+        got = pa.pa_cascade_plan(tab, lens, bs, 8 * G, 8, mp_min)
+        pre, groups, members, mp = _plan_by_definition(tab, lens, bs, G, mp_min)
+        assert got[0].tolist() == pre
+        assert got[1].tolist() == groups
+        assert got[2].tolist() == members
+        assert got[3] == mp
+    # every member of a group holds the same blocks for its prefix
+    pre, groups, members, _ = pa.pa_cascade_plan(tab, lens, bs, 8 * G, 8, 0)
+    for first, cnt, Lp in groups.tolist():
+        rows = [tab[m, :-(-Lp // bs)] for m in members[first:first + cnt]]
+        assert all((r == rows[0]).all() for r in rows) and all(lens[m] >= Lp for m in members[first:first + cnt])
