@@ -219,8 +219,8 @@ pa_status pa_decode_order(const int32_t* block_tables, int max_blocks_per_seq,
  * blocks for their first L tokens (forks, parallel samples, beams, prefix
  * cache hits; encyclopedia entry, "como funciona": shared prefixes are mapped,
  * not copied) can have that part attended in one pass for all of them: their
- * queries fill the 16 columns of the matrix-core tile (16 / G sequences of G
- * query heads each), so one read of each K/V block serves the whole group.
+ * queries fill two 16-column matrix-core tiles (32 / G sequences of G query
+ * heads each), so one read of each K/V block serves the whole group.
  * The rest of every context runs as in pa_decode, and the split-K reduce
  * merges both parts.  Same result as pa_decode up to floating-point rounding
  * order.
@@ -230,13 +230,15 @@ pa_status pa_decode_order(const int32_t* block_tables, int max_blocks_per_seq,
  * identical leading table entries, capped by the shortest member's context,
  * rounded down to a multiple of 32, and kept only when >= max(min_prefix, 32)
  * and the group has two or more members; groups are cut into column groups
- * of 16 / G members (none when G > 8).  Outputs: prefix_len_out[num_seqs]
+ * of 32 / G members (none when G > 16).  Outputs: prefix_len_out[num_seqs]
  * (L, or 0 for sequences outside any group), groups_out[num_seqs][3] =
  * {first member, member count, L}, members_out[num_seqs] (sequence indices),
- * *num_groups_out, *max_prefix_out.
+ * *num_groups_out, *max_prefix_out (largest L) and *max_members_out (largest
+ * member count).
  *
  * pa_decode_cascade: pa_decode plus that plan in device memory
- * (num_groups == 0 is plain pa_decode).  fp32 runs the plain path.  The
+ * (num_groups == 0 is plain pa_decode) and its two host values; groups of
+ * at most 16 / G members run one 16-column tile per load, larger ones two.  fp32 runs the plain path.  The
  * workspace must hold pa_decode_cascade_workspace_size(...) bytes, which is
  * non-zero even for an unsplit decode (the two parts meet in the reduce).
  */
@@ -244,7 +246,7 @@ pa_status pa_cascade_plan(const int32_t* block_tables, int max_blocks_per_seq,
                           const int32_t* context_lens, int num_seqs, int block_size,
                           int num_q_heads, int num_kv_heads, int min_prefix,
                           int32_t* prefix_len_out, int32_t* groups_out, int32_t* members_out,
-                          int* num_groups_out, int* max_prefix_out);
+                          int* num_groups_out, int* max_prefix_out, int* max_members_out);
 size_t pa_decode_cascade_workspace_size(int num_seqs, int num_q_heads, int head_dim,
                                         int max_context_len, int partition_size);
 pa_status pa_decode_cascade(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -254,8 +256,8 @@ pa_status pa_decode_cascade(void* out, const void* q, const void* k_cache, const
                             int head_dim, int block_size, int num_blocks, float scale,
                             int partition_size, const int32_t* prefix_len,
                             const int32_t* groups, const int32_t* members, int num_groups,
-                            int max_prefix, void* workspace, size_t workspace_bytes, int dtype,
-                            int flags, void* stream);
+                            int max_prefix, int max_members, void* workspace,
+                            size_t workspace_bytes, int dtype, int flags, void* stream);
 
 /*
  * pa_decode_step — one decode iteration of a batch as the central manager

@@ -21,6 +21,8 @@
 //
 // MFMA 16x16x32 operand layout (lane l, g = l / 16, c = l % 16):
 //   A[row c][k 8g..8g+7], B[k 8g..8g+7][col c], D[row 4g+r][col c], r = 0..3.
+#include <algorithm>
+
 #include "pa_internal.h"
 
 #ifndef PA_LAZY
@@ -101,14 +103,15 @@ __device__ __forceinline__ int chunks_of(int n, int part) {
 }
 
 // Token range of wave `wave` in chunk `ch` over tokens [lo, hi): partition
-// ch * NW + wave of `part` tokens, or with part == 0 an even split of the
-// range into NW runs of whole 32-token groups.
+// ch * NW + wave of `part` tokens; a range that fits one chunk (always with
+// part == 0) is split evenly into NW runs of whole 32-token groups, so that
+// no wave of the work-group idles.
 template <int NW>
 __device__ __forceinline__ ChunkSpan range_span(int lo, int hi, int part, int ch, int wave) {
   ChunkSpan sp;
   const int n = hi > lo ? hi - lo : 0;
   sp.nchunks = chunks_of<NW>(n, part);
-  const int unit = part > 0 ? part : (((n + NW - 1) / NW) + 31) & ~31;
+  const int unit = sp.nchunks > 1 ? part : (((n + NW - 1) / NW) + 31) & ~31;
   const int64_t a = (static_cast<int64_t>(ch) * NW + wave) * unit;
   sp.t0 = lo + (a < n ? static_cast<int>(a) : n);
   sp.t1 = lo + (a + unit < n ? static_cast<int>(a + unit) : n);
@@ -316,8 +319,19 @@ __device__ __forceinline__ void compute_group(GroupTiles<T, D>& G,
 //   kPrefix  one work-group per (chunk, KV head, column group): the sequences
 //            of a group share the physical blocks of their first L tokens, and
 //            their queries fill the 16 MFMA columns (member c / G, head c % G),
-//            so each K/V load serves all of them; partials only.
-enum { kPlain = 0, kSuffix = 1, kPrefix = 2 };
+//            so each K/V load serves all of them; partials only;
+//   kPrefix2 the same with two 16-column tiles per K/V load (groups of up to
+//            32 / G sequences).
+enum { kPlain = 0, kSuffix = 1, kPrefix = 2, kPrefix2 = 3 };
+
+// The prefix pass runs at most kPrefixWaves waves per work-group (its
+// two-tile form's registers allow two waves per SIMD), so its chunks count
+// with that many partitions.
+constexpr int kPrefixWaves = 4;
+template <int NW>
+struct PrefixNW {
+  static constexpr int value = NW > kPrefixWaves ? kPrefixWaves : NW;
+};
 
 // Cascade description on the device: prefix_len[B]; groups[ng][3] =
 // {first member, member count, L}; members[] = sequence indices.
@@ -329,7 +343,8 @@ struct Cascade {
 };
 
 template <typename T, int D, int BS, int NW, bool NT, int MODE>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PA_WAVES)))
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(MODE == kPrefix2 ? 2 : PA_WAVES)))
 void decode_part_mfma(
     T* __restrict__ out, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
@@ -347,25 +362,32 @@ void decode_part_mfma(
   const int c = lane & 15;  // MFMA row/column index within a lane group
   const int g = lane >> 4;  // lane group
   const WorkItem wi =
-      work_item<!NT>(blockIdx.x, H_kv * n_hg, MODE == kPrefix ? cas.ngroups : B, maxC);
+      work_item<!NT>(blockIdx.x, H_kv * n_hg, MODE >= kPrefix ? cas.ngroups : B, maxC);
   const int ch = wi.chunk;
   const int kvh = wi.hgl / n_hg;
   const int hg = wi.hgl - kvh * n_hg;
 
-  // the sequence whose table is read, this column's sequence and head, and
-  // the partial slot of chunk 0
-  int s, s_col, slot0 = 0, lo = 0, hi;
-  bool hvalid;
-  int hin;
-  if constexpr (MODE == kPrefix) {
+  // the sequence whose table is read, each tile column's sequence and head,
+  // and the partial slot of chunk 0; the prefix pass runs TT column tiles
+  // (TT x 16 columns) on every loaded K/V group
+  constexpr bool PREFIX = MODE == kPrefix || MODE == kPrefix2;
+  constexpr int TT = MODE == kPrefix2 ? 2 : 1;
+  int s, slot0 = 0, lo = 0, hi;
+  int s_col[TT], hin[TT];
+  bool hvalid[TT];
+  if constexpr (PREFIX) {
     const int gi = wi.seq;
     const int first = cas.groups[3 * gi], count = cas.groups[3 * gi + 1];
     hi = cas.groups[3 * gi + 2];
     s = cas.members[first];
-    const int mi = c / G;
-    hin = c - mi * G;
-    hvalid = mi < count;
-    s_col = hvalid ? cas.members[first + mi] : s;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      const int col = 16 * t + c;
+      const int mi = col / G;
+      hin[t] = col - mi * G;
+      hvalid[t] = mi < count;
+      s_col[t] = hvalid[t] ? cas.members[first + mi] : s;
+    }
   } else {
     s = order ? order[wi.seq] : wi.seq;
     if (s < 0 || s >= B) return;
@@ -374,36 +396,39 @@ void decode_part_mfma(
     if constexpr (MODE == kSuffix) {
       lo = cas.prefix_len[s];
       lo = lo < 0 ? 0 : (lo > hi ? hi : lo);
-      if (lo > 0) slot0 = chunks_of<NW>(lo, part);
+      if (lo > 0) slot0 = chunks_of<PrefixNW<NW>::value>(lo, part);
     }
-    hin = hg * 16 + c;  // head within the GQA group
-    hvalid = hin < G;
-    s_col = s;
+    hin[0] = hg * 16 + c;  // head within the GQA group
+    hvalid[0] = hin[0] < G;
+    s_col[0] = s;
   }
   const ChunkSpan sp = range_span<NW>(lo, hi, part, ch, wave);
   if (ch >= sp.nchunks) return;  // uniform over the work-group
   const int t0 = sp.t0, t1 = sp.t1;
-  const int qh = kvh * G + hin;
-  // the final output is written here only for a context in one chunk with no
-  // prefix pass
-  const bool final_out = MODE == kPlain ? sp.nchunks == 1
-                                        : (MODE == kSuffix && slot0 == 0 && sp.nchunks == 1);
+  // the final output is written here for a context in one chunk; a suffix in
+  // one chunk first merges the prefix pass's partials of its rows
+  const bool final_out = !PREFIX && sp.nchunks == 1;
 
-  // B operand of QK: Q[head c][dims 8(4k+g) .. +8] for chunk k.
-  v8 qop[NC];
+  // B operand of QK: Q[column c][dims 8(4k+g) .. +8] for chunk k.
+  v8 qop[TT][NC];
+  f32x4 o[TT][NJ];
+  float m[TT], l[TT];
 #pragma unroll
-  for (int k = 0; k < NC; ++k) {
-    if (hvalid)
-      qop[k] = *reinterpret_cast<const v8*>(q + (static_cast<int64_t>(s_col) * H_q + qh) * D +
-                                            (4 * k + g) * 8);
-    else
-      qop[k] = v8{};
+  for (int t = 0; t < TT; ++t) {
+    const int qh = kvh * G + hin[t];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      if (hvalid[t])
+        qop[t][k] = *reinterpret_cast<const v8*>(
+            q + (static_cast<int64_t>(s_col[t]) * H_q + qh) * D + (4 * k + g) * 8);
+      else
+        qop[t][k] = v8{};
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) o[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[t] = -INFINITY;
+    l[t] = 0.f;
   }
-
-  f32x4 o[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
 
   const int32_t* bt = block_tables + static_cast<int64_t>(s) * maxb;
   const int64_t blk_stride = static_cast<int64_t>(H_kv) * TILE;
@@ -434,73 +459,111 @@ void decode_part_mfma(
     GroupTiles<T, D> A;
     load_group<T, D, BS, NT>(A, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
                          vblk, vslab, g, c, lane);
-    compute_group<T, D, false>(A, qop, o, m, l, 32, g, scale_log2);
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+      compute_group<T, D, false>(A, qop[t], o[t], m[t], l[t], 32, g, scale_log2);
   }
   if (tg < t1) {
     GroupTiles<T, D> A;
     load_group<T, D, BS, NT>(A, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
                          vblk, vslab, g, c, lane);
-    compute_group<T, D, true>(A, qop, o, m, l, t1 - tg, g, scale_log2);
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+      compute_group<T, D, true>(A, qop[t], o[t], m[t], l[t], t1 - tg, g, scale_log2);
   }
 
-  float lt = xor_sum(l, 16);
-  lt = xor_sum(lt, 32);
+  float lt[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    lt[t] = xor_sum(l[t], 16);
+    lt[t] = xor_sum(lt[t], 32);
+  }
 
   if constexpr (NW > 1) {
     // Merge the waves' states: M = max m_w, weights 2^(m_w - M).
-    __shared__ float sh_m[NW][16];
-    __shared__ float sh_l[NW][16];
-    __shared__ f32x4 sh_o[NW - 1][NJ][64];
-    if (g == 0) {
-      sh_m[wave][c] = m;
-      sh_l[wave][c] = lt;
-    }
-    if (wave > 0) {
+    __shared__ float sh_m[NW][TT][16];
+    __shared__ float sh_l[NW][TT][16];
+    __shared__ f32x4 sh_o[NW - 1][TT][NJ][64];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) sh_o[wave - 1][j][lane] = o[j];
+    for (int t = 0; t < TT; ++t) {
+      if (g == 0) {
+        sh_m[wave][t][c] = m[t];
+        sh_l[wave][t][c] = lt[t];
+      }
+      if (wave > 0) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) sh_o[wave - 1][t][j][lane] = o[t][j];
+      }
     }
     __syncthreads();
     if (wave > 0) return;
-    float mw[NW];
-    float mm = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      mw[w] = sh_m[w][c];
-      mm = fmaxf(mm, mw[w]);
+    for (int t = 0; t < TT; ++t) {
+      float mw[NW];
+      float mm = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        mw[w] = sh_m[w][t][c];
+        mm = fmaxf(mm, mw[w]);
+      }
+      float f[NW];
+      float ls = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        f[w] = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - mm);
+        ls = fmaf(f[w], sh_l[w][t][c], ls);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        f32x4 acc = f[0] * o[t][j];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) acc += f[w] * sh_o[w - 1][t][j][lane];
+        o[t][j] = acc;
+      }
+      m[t] = mm;
+      lt[t] = ls;
     }
-    float f[NW];
-    float ls = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      f[w] = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - mm);
-      ls = fmaf(f[w], sh_l[w][c], ls);
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      f32x4 acc = f[0] * o[j];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) acc += f[w] * sh_o[w - 1][j][lane];
-      o[j] = acc;
-    }
-    m = mm;
-    lt = ls;
   }
 
-  if (!hvalid) return;
-  const int64_t row = static_cast<int64_t>(s_col) * H_q + qh;
-  if (final_out) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    T* dst = out + row * D + 4 * g;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+  for (int t = 0; t < TT; ++t) {
+    if (!hvalid[t]) continue;
+    const int64_t row = static_cast<int64_t>(s_col[t]) * H_q + kvh * G + hin[t];
+    if constexpr (MODE == kSuffix) {
+      if (final_out && slot0 > 0) {
+        // M = max over the prefix partials and this state, weights 2^(m_p - M)
+        const int64_t base = row * ws_stride;
+        float mm = m[t];
+        for (int p = 0; p < slot0; ++p) mm = fmaxf(mm, ws_ml[base + p].x);
+        const float fs = m[t] == -INFINITY ? 0.f : fast_exp2(m[t] - mm);
+        lt[t] *= fs;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[16 * j + r] = static_cast<T>(o[j][r] * inv);
-  } else {
-    const int64_t slot = row * ws_stride + slot0 + ch;
-    float* dst = ws_o + slot * D + 4 * g;
+        for (int j = 0; j < NJ; ++j) o[t][j] *= fs;
+        for (int p = 0; p < slot0; ++p) {
+          const float2 v = ws_ml[base + p];
+          const float f = v.x == -INFINITY ? 0.f : fast_exp2(v.x - mm);
+          lt[t] = fmaf(f, v.y, lt[t]);
+          const float* src = ws_o + (base + p) * D + 4 * g;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = o[j];
-    if (g == 0) ws_ml[slot] = make_float2(m, lt);
+          for (int j = 0; j < NJ; ++j)
+            o[t][j] += f * *reinterpret_cast<const f32x4*>(src + 16 * j);
+        }
+      }
+    }
+    if (final_out) {
+      const float inv = lt[t] > 0.f ? 1.f / lt[t] : 0.f;
+      T* dst = out + row * D + 4 * g;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[16 * j + r] = static_cast<T>(o[t][j][r] * inv);
+    } else {
+      const int64_t slot = row * ws_stride + slot0 + ch;
+      float* dst = ws_o + slot * D + 4 * g;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = o[t][j];
+      if (g == 0) ws_ml[slot] = make_float2(m[t], lt[t]);
+    }
   }
 }
 
@@ -648,7 +711,9 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce(
   int nchunks;
   if (prefix_len && prefix_len[s] > 0) {
     const int L = prefix_len[s] < ctx ? prefix_len[s] : ctx;
-    nchunks = chunks_of<NW>(L, part) + chunks_of<NW>(ctx - L, part);
+    const int nsuf = chunks_of<NW>(ctx - L, part);
+    if (nsuf == 1) return;  // merged by the suffix pass
+    nchunks = chunks_of<PrefixNW<NW>::value>(L, part) + nsuf;
   } else {
     nchunks = chunks_of<NW>(ctx, part);
     if (nchunks <= 1) return;
@@ -729,6 +794,7 @@ struct DecodeArgs {
   hipStream_t st;
   Cascade cas;           // ngroups > 0: prefix pass + suffix pass
   int max_prefix;        // longest group prefix
+  int max_members;       // largest group
 };
 
 template <typename T, int D, int BS, int NW, bool NT, int MODE>
@@ -767,16 +833,19 @@ void launch_mfma_nw(const DecodeArgs& a) {
   }
   // prefix pass (groups re-read the same blocks: cached loads), then the rest
   // of every sequence, then the merge; row stride maxC + 1 slots
-  const int stride = maxC + 1;
-  launch_part<T, D, BS, NW, false, kPrefix>(a, host_chunks(a.max_prefix, a.part, NW), stride,
-                                            a.cas.ngroups);
-  if (a.shared_kv)
-    launch_part<T, D, BS, NW, false, kSuffix>(a, maxC, stride, a.B);
+  // (the suffixes are mostly private blocks: streaming loads)
+  constexpr int NWP = PrefixNW<NW>::value;
+  const int stride = host_chunks(a.max_tokens, a.part, NWP) + 1;
+  const int cp = host_chunks(a.max_prefix, a.part, NWP);
+  if (a.max_members * a.G > 16)
+    launch_part<T, D, BS, NWP, false, kPrefix2>(a, cp, stride, a.cas.ngroups);
   else
-    launch_part<T, D, BS, NW, true, kSuffix>(a, maxC, stride, a.B);
-  hipLaunchKernelGGL((decode_reduce<T, D, NW>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0, a.st,
-                     static_cast<T*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens, a.H_q,
-                     a.part, stride, a.cas.prefix_len);
+    launch_part<T, D, BS, NWP, false, kPrefix>(a, cp, stride, a.cas.ngroups);
+  launch_part<T, D, BS, NW, true, kSuffix>(a, maxC, stride, a.B);
+  if (maxC > 1)  // some suffix may take several chunks
+    hipLaunchKernelGGL((decode_reduce<T, D, NW>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0,
+                       a.st, static_cast<T*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens,
+                       a.H_q, a.part, stride, a.cas.prefix_len);
 }
 
 // Waves per work-group for a partition size (see kChunkTokens).
@@ -829,7 +898,7 @@ PA_EXPORT size_t pa_decode_cascade_workspace_size(int num_seqs, int num_q_heads,
     return 0;
   const int maxP = num_partitions(max_context_len, partition_size);
   const int part = maxP > 1 ? partition_size : 0;
-  int nw = waves_per_group(part);
+  const int nw = std::min(waves_per_group(part), kPrefixWaves);
   const int stride = host_chunks(max_context_len, part, nw) + 1;
   const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * stride;
   const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
@@ -880,7 +949,9 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   const bool cascade = plan && plan->ngroups > 0 && dtype != PA_F32 &&
                        num_q_heads / num_kv_heads <= 16;
   if (cascade && (!plan->prefix_len || !plan->groups || !plan->members || plan->ngroups < 0 ||
-                  plan->max_prefix < 0 || plan->max_prefix > max_context_len))
+                  plan->max_prefix < 0 || plan->max_prefix > max_context_len ||
+                  plan->max_members < 1 ||
+                  plan->max_members * (num_q_heads / num_kv_heads) > 32))
     return PA_ERR_INVALID;
   const size_t need =
       cascade ? pa_decode_cascade_workspace_size(num_seqs, num_q_heads, head_dim,
@@ -911,11 +982,13 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   a.part = a.maxP > 1 ? partition_size : 0;
   a.cas = Cascade{nullptr, nullptr, nullptr, 0};
   a.max_prefix = 0;
+  a.max_members = 0;
   size_t slots = a.maxP;
   if (cascade) {
     a.cas = Cascade{plan->prefix_len, plan->groups, plan->members, plan->ngroups};
     a.max_prefix = plan->max_prefix;
-    slots = host_chunks(max_context_len, a.part, waves_per_group(a.part)) + 1;
+    a.max_members = plan->max_members;
+    slots = host_chunks(max_context_len, a.part, std::min(waves_per_group(a.part), kPrefixWaves)) + 1;
   }
   if (need > 0) {
     const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * slots;
@@ -964,11 +1037,11 @@ PA_EXPORT pa_status pa_decode_cascade(void* out, const void* q, const void* k_ca
                                       int block_size, int num_blocks, float scale,
                                       int partition_size, const int32_t* prefix_len,
                                       const int32_t* groups, const int32_t* members,
-                                      int num_groups, int max_prefix, void* workspace,
-                                      size_t workspace_bytes, int dtype, int flags,
-                                      void* stream) {
+                                      int num_groups, int max_prefix, int max_members,
+                                      void* workspace, size_t workspace_bytes, int dtype,
+                                      int flags, void* stream) {
   if (num_groups < 0) return PA_ERR_INVALID;
-  const CascadePlan plan{prefix_len, groups, members, num_groups, max_prefix};
+  const CascadePlan plan{prefix_len, groups, members, num_groups, max_prefix, max_members};
   return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, flags,

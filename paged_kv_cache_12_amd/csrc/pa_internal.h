@@ -35,13 +35,15 @@ inline pa_status launch_status() {
 
 // Shared-prefix (cascade) plan, device arrays: prefix_len[num_seqs],
 // groups[ngroups][3] = {first member, member count, prefix tokens},
-// members[] = sequence indices; max_prefix = largest prefix (host value).
+// members[] = sequence indices; max_prefix = largest prefix, max_members =
+// largest group (host values).
 struct CascadePlan {
   const int32_t* prefix_len;
   const int32_t* groups;
   const int32_t* members;
   int ngroups;
   int max_prefix;
+  int max_members;
 };
 
 // pa_decode with an optional sequence order (a permutation of 0..num_seqs-1,

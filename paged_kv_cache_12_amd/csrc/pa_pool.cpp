@@ -511,18 +511,20 @@ PA_EXPORT pa_status pa_cascade_plan(const int32_t* block_tables, int max_blocks_
                                     int num_q_heads, int num_kv_heads, int min_prefix,
                                     int32_t* prefix_len_out, int32_t* groups_out,
                                     int32_t* members_out, int* num_groups_out,
-                                    int* max_prefix_out) {
+                                    int* max_prefix_out, int* max_members_out) {
   if (num_seqs < 0 || max_blocks_per_seq < 0 || block_size <= 0 || num_q_heads <= 0 ||
-      num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || !num_groups_out || !max_prefix_out)
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || !num_groups_out ||
+      !max_prefix_out || !max_members_out)
     return PA_ERR_INVALID;
   *num_groups_out = 0;
   *max_prefix_out = 0;
+  *max_members_out = 0;
   if (num_seqs == 0) return PA_OK;
   if (!block_tables || !context_lens || !prefix_len_out || !groups_out || !members_out)
     return PA_ERR_INVALID;
   for (int s = 0; s < num_seqs; ++s) prefix_len_out[s] = 0;
   const int G = num_q_heads / num_kv_heads;
-  const int cap = G <= 16 ? 16 / G : 0;  // sequences per 16 MFMA columns
+  const int cap = G <= 16 ? 32 / G : 0;  // sequences per 2 x 16 MFMA columns
   if (cap < 2 || max_blocks_per_seq == 0) return PA_OK;
   // families: sequences whose tables start with the same physical block, in
   // order of first appearance, members in index order
@@ -561,6 +563,7 @@ PA_EXPORT pa_status pa_cascade_plan(const int32_t* block_tables, int max_blocks_
         members_out[nm++] = f[i + k];
         prefix_len_out[f[i + k]] = L;
       }
+      *max_members_out = std::max(*max_members_out, cnt);
       ++ng;
     }
     *max_prefix_out = std::max(*max_prefix_out, L);

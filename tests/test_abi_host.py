@@ -323,9 +323,9 @@ def _plan_by_definition(tab, lens, bs, G, min_prefix):
     B = len(lens)
     pre = [0] * B
     groups, members = [], []
-    cap = 16 // G if G <= 16 else 0
+    cap = 32 // G if G <= 16 else 0
     if cap < 2:
-        return pre, groups, members, 0
+        return pre, groups, members, 0, 0
     fams, order = {}, []
     for s in range(B):
         if lens[s] <= 0 or tab[s][0] < 0:
@@ -334,7 +334,7 @@ def _plan_by_definition(tab, lens, bs, G, min_prefix):
             fams[tab[s][0]] = []
             order.append(tab[s][0])
         fams[tab[s][0]].append(s)
-    mp = 0
+    mp, mm = 0, 0
     for key in order:
         f = fams[key]
         if len(f) < 2:
@@ -350,11 +350,12 @@ def _plan_by_definition(tab, lens, bs, G, min_prefix):
         for i in range(0, len(f), cap):
             part = f[i:i + cap]
             groups.append([len(members), len(part), L])
+            mm = max(mm, len(part))
             members += part
             for s in part:
                 pre[s] = L
         mp = max(mp, L)
-    return pre, groups, members, mp
+    return pre, groups, members, mp, mm
 
 
 @pytest.mark.parametrize("seed,G", [(0, 4), (1, 1), (2, 8), (3, 16), (4, 2)])
@@ -372,13 +373,13 @@ def test_cascade_plan_matches_its_definition(L, seed, G):
         tab[s, :nb] = row
     for mp_min in (0, 64, 512):
         got = pa.pa_cascade_plan(tab, lens, bs, 8 * G, 8, mp_min)
-        pre, groups, members, mp = _plan_by_definition(tab, lens, bs, G, mp_min)
+        pre, groups, members, mp, mm = _plan_by_definition(tab, lens, bs, G, mp_min)
         assert got[0].tolist() == pre
         assert got[1].tolist() == groups
         assert got[2].tolist() == members
-        assert got[3] == mp
+        assert got[3] == mp and got[4] == mm
     # every member of a group holds the same blocks for its prefix
-    pre, groups, members, _ = pa.pa_cascade_plan(tab, lens, bs, 8 * G, 8, 0)
+    pre, groups, members, _, _ = pa.pa_cascade_plan(tab, lens, bs, 8 * G, 8, 0)
     for first, cnt, Lp in groups.tolist():
         rows = [tab[m, :-(-Lp // bs)] for m in members[first:first + cnt]]
         assert all((r == rows[0]).all() for r in rows) and all(lens[m] >= Lp for m in members[first:first + cnt])

@@ -62,7 +62,8 @@ def test_cascade_decode_matches_oracle(name, part):
     H.execute(sc, os_)
     seqs = sc.decode_seqs
     tab, lens = gs.cache.tables(seqs)
-    pre, groups, members, mp = pa.pa_cascade_plan(tab, lens, wl.block_size, wl.h_q, wl.h_kv, 64)
+    pre, groups, members, mp, mm = pa.pa_cascade_plan(tab, lens, wl.block_size, wl.h_q, wl.h_kv,
+                                                      64)
     assert len(groups) > 0 and mp > 0
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q = storage_to_torch(sc.q, wl.dtype).cuda()
@@ -73,7 +74,7 @@ def test_cascade_decode_matches_oracle(name, part):
     order = dev(pa.pa_decode_order(tab, lens))
     out = torch.empty_like(q)
     pa.pa_decode_cascade(out, q, gs.cache.k_cache, gs.cache.v_cache, dev(tab), dev(lens), max_ctx,
-                         wl.scale, part, dev(pre), dev(groups.reshape(-1)), dev(members), mp, ws,
+                         wl.scale, part, dev(pre), dev(groups.reshape(-1)), dev(members), mp, mm, ws,
                          flags=pa.PA_DECODE_SHARED_KV, seq_order=order)
     plain = torch.empty_like(q)
     ws2 = torch.zeros(max(256, pa.pa_decode_workspace_size(len(seqs), wl.h_q, wl.head_dim,
@@ -91,7 +92,7 @@ def test_cascade_decode_matches_oracle(name, part):
     again = torch.empty_like(q)
     pa.pa_decode_cascade(again, q, gs.cache.k_cache, gs.cache.v_cache, dev(tab), dev(lens),
                          max_ctx, wl.scale, part, dev(pre), dev(groups.reshape(-1)),
-                         dev(members), mp, ws, flags=pa.PA_DECODE_SHARED_KV, seq_order=order)
+                         dev(members), mp, mm, ws, flags=pa.PA_DECODE_SHARED_KV, seq_order=order)
     torch.cuda.synchronize()
     assert torch.equal(again.view(torch.int16), out.view(torch.int16))
 
@@ -112,9 +113,9 @@ def test_cascade_with_no_groups_is_plain_decode():
                          pa.pa_decode_workspace_size(B, wl.h_q, wl.head_dim, mc, 512)),
                      dtype=torch.uint8, device="cuda")
     a, b = torch.empty_like(q), torch.empty_like(q)
-    empty = torch.zeros(3, dtype=torch.int32, device="cuda")
+    empty = torch.zeros(0, dtype=torch.int32, device="cuda")
     pa.pa_decode_cascade(a, q, gs.cache.k_cache, gs.cache.v_cache, dev(tab), dev(lens), mc,
-                         wl.scale, 512, dev(np.zeros(B, np.int32)), empty, empty[:1], 0, ws)
+                         wl.scale, 512, dev(np.zeros(B, np.int32)), empty, empty, 0, 0, ws)
     pa.pa_decode(b, q, gs.cache.k_cache, gs.cache.v_cache, dev(tab), dev(lens), mc, wl.scale,
                  512, workspace=ws)
     torch.cuda.synchronize()
@@ -143,7 +144,7 @@ def test_decode_step_uses_the_cascade_for_long_shared_prefixes(dtype, part):
     B = len(seqs)
     maxb = 64
     tab, ln = os_.tables(list(seqs))
-    pre, groups, members, mp = pa.pa_cascade_plan(tab, ln + 1, bs, H_q, H_kv, 512)
+    pre, groups, members, mp, _ = pa.pa_cascade_plan(tab, ln + 1, bs, H_q, H_kv, 512)
     assert len(groups) == 2 and mp == 896          # the step's plan: two families
     sbytes = pa.pa_decode_step_staging_size(B, maxb)
     hs = [torch.empty(sbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
