@@ -446,7 +446,10 @@ def bench_beam(args, width: int = 4):
     h_stage = [torch.empty(sbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
     d_stage = torch.empty(sbytes, dtype=torch.uint8, device=dev)
     ws = torch.zeros(max(256, pa.pa_decode_workspace_size(B, wl.h_q, wl.head_dim,
-                                                          plen + steps_total + 1, wl.partition)),
+                                                          plen + steps_total + 1, wl.partition),
+                         pa.pa_decode_cascade_workspace_size(B, wl.h_q, wl.head_dim,
+                                                             plen + steps_total + 1,
+                                                             wl.partition)),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     done = [None, None]
