@@ -213,15 +213,15 @@ __device__ __forceinline__ void load_group(GroupTiles<T, D>& G, TableWindow& w,
   for (int j = 0; j < NJ; ++j) G.v[j] = load16<v8, NT>(base + 16 * j * 8);
 }
 
-// QK, online-softmax update and PV for one 32-token group.  TAIL: only the
-// first `rem` tokens of the group are inside the context (the last group of a
-// partition); the others are masked out of the scores and their V operands
-// are zeroed, since slots past the fill may hold anything (0 * NaN = NaN).
+// QK and the online-softmax update for one 32-token group; returns the
+// weights as the PV B operand.  TAIL: only the first `rem` tokens of the group
+// are inside the context (the last group of a range); the others are masked
+// out of the scores.
 template <typename T, int D, bool TAIL>
-__device__ __forceinline__ void compute_group(GroupTiles<T, D>& G,
-                                              const typename Mfma<T>::v8* qop, f32x4* o,
-                                              float& m, float& l, int rem, int g,
-                                              float scale_log2) {
+__device__ __forceinline__ typename Mfma<T>::v8 qk_softmax(const GroupTiles<T, D>& G,
+                                                           const typename Mfma<T>::v8* qop,
+                                                           f32x4* o, float& m, float& l, int rem,
+                                                           int g, float scale_log2) {
   typedef Mfma<T> M;
   typedef typename M::v8 v8;
   constexpr int NC = D / 32, NJ = D / 16;
@@ -286,6 +286,17 @@ __device__ __forceinline__ void compute_group(GroupTiles<T, D>& G,
 #pragma unroll
   for (int j = 0; j < NJ; ++j) o[j] *= alpha;
 #endif
+  return pop;
+}
+
+// PV for one 32-token group.  TAIL: V lanes of tokens past `rem` are zeroed
+// first, since slots past the fill may hold anything (0 * NaN = NaN).
+template <typename T, int D, bool TAIL>
+__device__ __forceinline__ void pv(GroupTiles<T, D>& G, typename Mfma<T>::v8 pop, f32x4* o,
+                                   int rem, int g) {
+  typedef Mfma<T> M;
+  typedef typename M::v8 v8;
+  constexpr int NJ = D / 16;
   if (TAIL) {
     // keep the first nv of this lane's 8 V elements (16-bit lanes of 4 dwords)
     const int nv = rem - 8 * g;
@@ -304,13 +315,16 @@ __device__ __forceinline__ void compute_group(GroupTiles<T, D>& G,
   for (int j = 0; j < NJ; ++j) o[j] = M::mma(G.v[j], pop, o[j]);
 }
 
-// One work-group of NW wavefronts per (chunk, KV head [x head group],
-// sequence).  A chunk is NW consecutive partitions; wave w runs partition
-// chunk * NW + w with its own running state, and the NW states are merged
-// (log-sum-exp) in LDS, so one partial per chunk goes to memory.  Writes in
-// the middle of the KV read stream are expensive on this part (a few KiB per
-// work unit cost up to ~18 % of bandwidth), hence one write per NW partitions.
-// With part == 0 the context is one chunk split evenly across the waves.
+// QK, online-softmax update and PV for one 32-token group.
+template <typename T, int D, bool TAIL>
+__device__ __forceinline__ void compute_group(GroupTiles<T, D>& G,
+                                              const typename Mfma<T>::v8* qop, f32x4* o,
+                                              float& m, float& l, int rem, int g,
+                                              float scale_log2) {
+  const typename Mfma<T>::v8 pop = qk_softmax<T, D, TAIL>(G, qop, o, m, l, rem, g, scale_log2);
+  pv<T, D, TAIL>(G, pop, o, rem, g);
+}
+
 // Work decomposition of decode_part_mfma:
 //   kPlain   one work-group per (chunk, KV head [x head group], sequence);
 //   kSuffix  the same over tokens [prefix_len[s], ctx) of each sequence, always
