@@ -266,13 +266,19 @@ pa_status pa_decode_cascade(void* out, const void* q, const void* k_cache, const
  * of seqs[0..num_seqs) in the pool, build slots, copy-on-write pairs, lengths
  * and block tables in `host_staging`, copy them to `dev_staging` with one
  * asynchronous host-to-device copy, then run pa_copy_blocks (if any pair),
- * pa_write_kv of k_new / v_new (device [num_seqs][H_kv][d]) into the new
+ * the block write of k_new / v_new (device [num_seqs][H_kv][d]) into the new
  * positions, and pa_decode of q into out (device [num_seqs][H_q][d]).  The
  * decode issues the sequences in pa_decode_order's order and sets
  * PA_DECODE_SHARED_KV itself whenever the pool holds a block with
  * refcount > 1; then, if the workspace holds
  * pa_decode_cascade_workspace_size(...) bytes, shared prefixes of 512 tokens
  * or more go through the cascade (pa_cascade_plan).
+ *
+ * For fp16 / bf16 the block write runs inside the decode launch: the wave
+ * that ends each context takes the appended token from k_new / v_new for its
+ * last group and stores it in its slot (fp32 runs pa_write_kv first).  All
+ * work is on `stream`.  Not for graph capture (the pool step runs on the
+ * host).
  *
  *   host_staging  pinned host memory (hipHostMalloc), >=
  *                 pa_decode_step_staging_size() bytes, 16-byte aligned; a
@@ -302,9 +308,10 @@ pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_seqs, const
 /*
  * pa_beam_decode_step — one beam-search iteration in one call:
  * pa_seq_beam_step(old_beams, parents, new_beams) in the pool, then, as in
- * pa_decode_step, the staging copy, pa_copy_blocks of its pairs, pa_write_kv of
- * k_new / v_new (device [n_new][H_kv][d], in new_beams order) and pa_decode of
- * q into out (device [n_new][H_q][d]).  Staging sized by
+ * pa_decode_step (same staging and fused block write), the staging
+ * copy, pa_copy_blocks of its pairs, the block write of k_new / v_new (device
+ * [n_new][H_kv][d], in new_beams order) and pa_decode of q into out (device
+ * [n_new][H_q][d]).  Staging sized by
  * pa_decode_step_staging_size(n_new, max_blocks_per_seq).  Shapes, buffers,
  * table capacity and workspace are checked before the pool changes; the
  * pool step's own rules (and its PA_ERR_NO_BLOCKS behaviour) are those of

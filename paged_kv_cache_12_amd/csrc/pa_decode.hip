@@ -23,7 +23,7 @@
 //   A[row c][k 8g..8g+7], B[k 8g..8g+7][col c], D[row 4g+r][col c], r = 0..3.
 #include <algorithm>
 
-#include "pa_internal.h"
+#include "pa_kv_store.h"
 
 #ifndef PA_LAZY
 #define PA_LAZY 1
@@ -315,6 +315,43 @@ __device__ __forceinline__ void pv(GroupTiles<T, D>& G, typename Mfma<T>::v8 pop
   for (int j = 0; j < NJ; ++j) o[j] = M::mma(G.v[j], pop, o[j]);
 }
 
+// Replaces token u (0..31) of a loaded group by the appended token's K row
+// and V column (k_row / v_col: its D values): the K rows of MFMA half h hold
+// token 8(c/4) + 4h + c%4 in lane c, and V lane group g holds tokens
+// 8g .. 8g+7 of dims 16j + c.
+template <typename T, int D>
+__device__ __forceinline__ void patch_new_token(GroupTiles<T, D>& G, const T* k_row,
+                                                const T* v_col, int u, int g, int c) {
+  typedef typename Mfma<T>::v8 v8;
+  constexpr int NC = D / 32, NJ = D / 16;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (8 * (c >> 2) + 4 * h + (c & 3) == u) {
+#pragma unroll
+      for (int k = 0; k < NC; ++k)
+        G.k[h][k] = *reinterpret_cast<const v8*>(k_row + (4 * k + g) * 8);
+    }
+  }
+  if ((u >> 3) == g) {
+    // element u % 8 of each V vector: 16-bit half (u & 1) of dword (u & 7) / 2
+    // (selects over constant indices keep the vectors in registers)
+    const int w = (u & 7) >> 1;
+    const bool hi_half = u & 1;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint32_t val = __builtin_bit_cast(uint16_t, v_col[16 * j + c]);
+      u32x4 bits = __builtin_bit_cast(u32x4, G.v[j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t put = hi_half ? ((bits[i] & 0x0000FFFFu) | (val << 16))
+                                     : ((bits[i] & 0xFFFF0000u) | val);
+        bits[i] = i == w ? put : bits[i];
+      }
+      G.v[j] = __builtin_bit_cast(v8, bits);
+    }
+  }
+}
+
 // QK, online-softmax update and PV for one 32-token group.
 template <typename T, int D, bool TAIL>
 __device__ __forceinline__ void compute_group(GroupTiles<T, D>& G,
@@ -361,10 +398,11 @@ __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(MODE == kPrefix2 ? 2 : PA_WAVES)))
 void decode_part_mfma(
     T* __restrict__ out, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
-    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const T* __restrict__ q, const T* kc, const T* vc,
     const int32_t* __restrict__ block_tables, int maxb, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ order, int B, int max_tokens, int H_q, int H_kv, int G,
-    int n_hg, int num_blocks, float scale_log2, int part, int maxC, int ws_stride, Cascade cas) {
+    int n_hg, int num_blocks, float scale_log2, int part, int maxC, int ws_stride, Cascade cas,
+    NewKV nkv) {
   typedef Mfma<T> M;
   typedef typename M::v8 v8;
   constexpr int NC = D / 32;    // QK k-chunks of 32 dims
@@ -463,8 +501,10 @@ void decode_part_mfma(
   const int vblk = (8 * g) / BS;
   const int vslab = ((8 * g) % BS) / 8;
 
-  // Full 32-token groups, then at most one partial group at the end.
-  const int tfull = t0 + ((t1 - t0) & ~31);
+  // Full 32-token groups, then at most one partial group at the end; with an
+  // appended token, the group holding it is always that last one.
+  const bool has_new = !PREFIX && nkv.k != nullptr && t0 < t1 && t1 == hi;
+  const int tfull = t0 + ((t1 - t0 - (has_new ? 1 : 0)) & ~31);
   const int nb_valid = (t1 + BS - 1) / BS;  // table entries inside the context
   TableWindow win;
   fill_window(win, bt, t0 / BS, nb_valid, num_blocks, lane);
@@ -481,9 +521,25 @@ void decode_part_mfma(
     GroupTiles<T, D> A;
     load_group<T, D, BS, NT>(A, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
                          vblk, vslab, g, c, lane);
+    if (has_new) {
+      const int64_t src = (static_cast<int64_t>(s) * H_kv + kvh) * D;
+      patch_new_token<T, D>(A, static_cast<const T*>(nkv.k) + src,
+                            static_cast<const T*>(nkv.v) + src, hi - 1 - tg, g, c);
+    }
 #pragma unroll
     for (int t = 0; t < TT; ++t)
       compute_group<T, D, true>(A, qop[t], o[t], m[t], l[t], t1 - tg, g, scale_log2);
+    if (has_new && lane < D * static_cast<int>(sizeof(T)) / 16) {
+      // the block write of the appended token (lane = 16-byte vector)
+      const int lb = (hi - 1) / BS;
+      const int32_t b = bt[lb];
+      if (b >= 0 && b < num_blocks)
+        store_token_vec<uint16_t>(static_cast<const uint16_t*>(nkv.k),
+                                  static_cast<const uint16_t*>(nkv.v),
+                                  reinterpret_cast<uint16_t*>(const_cast<T*>(kc)),
+                                  reinterpret_cast<uint16_t*>(const_cast<T*>(vc)), s, kvh, lane,
+                                  static_cast<int64_t>(b) * BS + (hi - 1) % BS, H_kv, D, BS);
+    }
   }
 
   float lt[TT];
@@ -809,6 +865,7 @@ struct DecodeArgs {
   Cascade cas;           // ngroups > 0: prefix pass + suffix pass
   int max_prefix;        // longest group prefix
   int max_members;       // largest group
+  NewKV nkv;             // the step's appended K/V, or nulls
 };
 
 template <typename T, int D, int BS, int NW, bool NT, int MODE>
@@ -821,7 +878,7 @@ void launch_part(const DecodeArgs& a, int maxC, int ws_stride, int nitems) {
                      static_cast<T*>(a.out), a.ws_o, a.ws_ml, static_cast<const T*>(a.q),
                      static_cast<const T*>(a.kc), static_cast<const T*>(a.vc), a.bt, a.maxb,
                      a.lens, a.order, a.B, a.max_tokens, a.H_q, a.H_kv, a.G, n_hg, a.num_blocks,
-                     a.scale_log2, a.part, maxC, ws_stride, a.cas);
+                     a.scale_log2, a.part, maxC, ws_stride, a.cas, a.nkv);
 }
 
 // Partial slots per (sequence, query head) row.
@@ -939,7 +996,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                       int num_blocks, float scale, int partition_size, void* workspace,
                       size_t workspace_bytes, int dtype, int flags, const int32_t* order,
-                      void* stream, const CascadePlan* plan) {
+                      void* stream, const CascadePlan* plan, const NewKV* nkv) {
   if (elem_bytes(dtype) == 0) return PA_ERR_UNSUPPORTED;
   if (flags & ~PA_DECODE_SHARED_KV) return PA_ERR_INVALID;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
@@ -997,6 +1054,11 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   a.cas = Cascade{nullptr, nullptr, nullptr, 0};
   a.max_prefix = 0;
   a.max_members = 0;
+  a.nkv = NewKV{nullptr, nullptr};
+  if (nkv && nkv->k && nkv->v && dtype != PA_F32) {
+    if (!aligned16(nkv->k) || !aligned16(nkv->v)) return PA_ERR_INVALID;
+    a.nkv = *nkv;
+  }
   size_t slots = a.maxP;
   if (cascade) {
     a.cas = Cascade{plan->prefix_len, plan->groups, plan->members, plan->ngroups};
@@ -1040,7 +1102,7 @@ PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* k_cache, con
   return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, flags,
-                     seq_order, stream, nullptr);
+                     seq_order, stream, nullptr, nullptr);
 }
 
 PA_EXPORT pa_status pa_decode_cascade(void* out, const void* q, const void* k_cache,
@@ -1059,5 +1121,5 @@ PA_EXPORT pa_status pa_decode_cascade(void* out, const void* q, const void* k_ca
   return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, flags,
-                     seq_order, stream, &plan);
+                     seq_order, stream, &plan, nullptr);
 }

@@ -46,15 +46,26 @@ struct CascadePlan {
   int max_members;
 };
 
+// The step's appended K/V ([num_seqs][H_kv][head_dim], device; fp16 / bf16),
+// or nulls: position ctx - 1 of every sequence is the token appended this
+// step, not yet in the cache.  The decode wave whose range ends at the
+// context patches it into its last group from here and stores it in its
+// cache slot (the block write fused into the decode); nothing in the same
+// launch reads that slot from memory.
+struct NewKV {
+  const void* k;
+  const void* v;
+};
+
 // pa_decode with an optional sequence order (a permutation of 0..num_seqs-1,
 // device memory; work-groups are issued in that order) and an optional
-// cascade plan.
+// cascade plan and, on the fp16 / bf16 path, the step's appended K/V.
 pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, int max_blocks_per_seq,
                       const int32_t* context_lens, int num_seqs, int max_context_len,
                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                       int num_blocks, float scale, int partition_size, void* workspace,
                       size_t workspace_bytes, int dtype, int flags, const int32_t* order,
-                      void* stream, const CascadePlan* plan);
+                      void* stream, const CascadePlan* plan, const NewKV* nkv);
 
 }  // namespace pa

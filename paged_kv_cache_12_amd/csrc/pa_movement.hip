@@ -2,14 +2,14 @@
 // first and third of the three custom kernels named in the vLLM encyclopedia
 // entry (tonho.wtf), section "o que isso custou".  Pure data movement: element
 // bits are moved, never converted.
-#include "pa_internal.h"
+#include "pa_kv_store.h"
 
 namespace pa {
 
 // One thread per 16-byte vector of one (token, head): the K vector lands as a
 // single 16-byte store in the token's row of a K slab; the V vector's x
-// elements are scattered to x consecutive V slab rows (dims), position t % x.
-// E is the element storage type (uint16_t for fp16/bf16, uint32_t for fp32).
+// elements are scattered to x consecutive V slab rows (dims), position t % x
+// (store_token_vec).  E is the element storage type.
 template <typename E>
 __global__ __launch_bounds__(256) void write_kv_kernel(const E* __restrict__ k_new,
                                                        const E* __restrict__ v_new,
@@ -28,24 +28,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const E* __restrict__ k_n
     const int64_t t = th / H;
     const int64_t slot = slots[t];
     if (slot < 0 || slot >= num_slots) continue;
-    const int64_t b = slot / BS;
-    const int tt = static_cast<int>(slot - b * BS);
-    const int64_t src = (t * H + h) * D + jv * X;
-    const int64_t tile = (b * H + h) * static_cast<int64_t>(BS) * D;
-    // K(b, h, tt, i) at tile + ((i / X) * BS + r(tt)) * X + i % X, where r puts
-    // the tokens with bit 2 clear first in each slab
-    const int kr = ((tt & 4) ? BS / 2 : 0) + 4 * (tt >> 3) + (tt & 3);
-    *reinterpret_cast<u32x4*>(kc + tile + (static_cast<int64_t>(jv) * BS + kr) * X) =
-        *reinterpret_cast<const u32x4*>(k_new + src);
-    // V(b, h, tt, i) at tile + ((tt / X) * D + i) * X + tt % X
-    union {
-      u32x4 v;
-      E e[X];
-    } vals;
-    vals.v = *reinterpret_cast<const u32x4*>(v_new + src);
-    E* vdst = vc + tile + (static_cast<int64_t>(tt / X) * D + jv * X) * X + tt % X;
-#pragma unroll
-    for (int e = 0; e < X; ++e) vdst[e * X] = vals.e[e];
+    store_token_vec<E>(k_new, v_new, kc, vc, t, h, jv, slot, H, D, BS);
   }
 }
 

@@ -3,14 +3,15 @@
 // ships the block tables with each iteration's input; beam candidates share
 // blocks and the sharing changes every step).  Host side: the pool step
 // (append, or beam fork / retire / append), tables and lengths into one pinned
-// staging buffer; device side: one host-to-device copy, then copy-on-write
-// copies, the block write and decode, all on the caller's stream.
+// staging buffer; device side, all on the caller's stream: one host-to-device
+// copy, copy-on-write copies and the decode, which also stores the step's new
+// K/V (fp16 / bf16; fp32 runs the block write before it).
 #include <algorithm>
 #include <cstring>
 #include <numeric>
 #include <vector>
 
-#include "pa_internal.h"
+#include "pa_kv_store.h"
 
 extern "C" int64_t pa_pool_shared_blocks(const pa_pool* p);
 
@@ -122,7 +123,7 @@ pa_status check_growth(const StepDev& a, int n, const int* nb, const int* ctx) {
 
 // After the pool has given slots and pairs (already in the staging buffer):
 // tables, lengths and issue order into staging, one host-to-device copy, then
-// copy-on-write, block write and decode on the stream.
+// copy-on-write and the decode with its block write on the stream.
 pa_status launch_step(pa_pool* pool, const StepDev& a, const int64_t* seqs, int n, int npairs) {
   const StagingLayout L = staging_layout(n, a.max_blocks_per_seq);
   char* h = static_cast<char*>(a.host_staging);
@@ -156,6 +157,15 @@ pa_status launch_step(pa_pool* pool, const StepDev& a, const int64_t* seqs, int 
     if (st != PA_OK) return st;
   }
 
+  // the block write rides in the decode (fp16 / bf16): the decode wave that
+  // ends a context takes the appended token from k_new / v_new; a shared
+  // prefix never reaches the appended position (its block is private)
+  bool fused_write = a.dtype != PA_F32;
+  if (plan.ngroups > 0) {
+    const int32_t* pre = reinterpret_cast<const int32_t*>(h + L.prefix);
+    for (int i = 0; i < n && fused_write; ++i) fused_write = pre[i] < h_lens[i];
+  }
+
   // one host-to-device copy of slots, pairs, lengths, order and tables: a
   // copy kernel reading the pinned buffer when it is mapped on the device,
   // else an asynchronous copy
@@ -177,16 +187,19 @@ pa_status launch_step(pa_pool* pool, const StepDev& a, const int64_t* seqs, int 
                         a.stream);
     if (st != PA_OK) return st;
   }
-  st = pa_write_kv(a.k_new, a.v_new, a.k_cache, a.v_cache,
-                   reinterpret_cast<const int64_t*>(d + L.slots), n, a.num_blocks,
-                   a.num_kv_heads, a.head_dim, a.block_size, a.dtype, a.stream);
-  if (st != PA_OK) return st;
+  if (!fused_write) {
+    st = pa_write_kv(a.k_new, a.v_new, a.k_cache, a.v_cache,
+                     reinterpret_cast<const int64_t*>(d + L.slots), n, a.num_blocks,
+                     a.num_kv_heads, a.head_dim, a.block_size, a.dtype, a.stream);
+    if (st != PA_OK) return st;
+  }
+  const NewKV nkv{fused_write ? a.k_new : nullptr, fused_write ? a.v_new : nullptr};
   return decode_impl(a.out, a.q, a.k_cache, a.v_cache,
                      reinterpret_cast<const int32_t*>(d + L.tables), a.max_blocks_per_seq,
                      reinterpret_cast<const int32_t*>(d + L.lens), n, max_ctx, a.num_q_heads,
                      a.num_kv_heads, a.head_dim, a.block_size, a.num_blocks, a.scale,
                      a.partition_size, a.workspace, a.workspace_bytes, a.dtype, flags,
-                     reinterpret_cast<const int32_t*>(d + L.order), a.stream, &plan);
+                     reinterpret_cast<const int32_t*>(d + L.order), a.stream, &plan, &nkv);
 }
 
 }  // namespace

@@ -332,6 +332,68 @@ def test_decode_step_matches_oracle(dtype, part):
     assert_caches_equal(gs, os_)
 
 
+@pytest.mark.parametrize("dtype,part,dev_buffers", [("bf16", 0, 2), ("f16", 64, 1),
+                                                    ("bf16", 32, 2), ("f32", 0, 2)])
+def test_decode_steps_back_to_back(dtype, part, dev_buffers):
+    """Steps enqueued without waiting for the GPU in between: each step's
+    staging copy runs on the library's side stream while the previous step's
+    kernels may still run.  Every step's output and the final caches must
+    match the oracle replaying the same appends."""
+    import torch
+    import paged_kv_cache_12_amd as pa
+    from paged_kv_cache_12_amd.manager import storage_to_torch
+    say("decode_steps_back_to_back", dtype, part, dev_buffers)
+    H_q, H_kv, d, bs = 8, 2, 64 if dtype == "f32" else 128, 16
+    lens = [1, 15, 16, 33, 200, 31]
+    sc = small_scenario(dtype, H_q, H_kv, d, bs, seed=6262 + part, lens=lens)
+    sc.ops += [("fork", 3, 6)]        # a shared, partly filled last block
+    sc.decode_seqs = [0, 1, 2, 3, 4, 5, 6]
+    sc.num_blocks += 24
+    sc.free_order = np.random.default_rng(2).permutation(sc.num_blocks).astype(np.int32)
+    gs, os_ = H.GpuSide(sc), H.OracleSide(sc)
+    H.execute(sc, gs)
+    H.execute(sc, os_)
+    seqs = np.array(sc.decode_seqs, dtype=np.int64)
+    B = len(seqs)
+    maxb = 32
+    nsteps = 12
+    sbytes = pa.pa_decode_step_staging_size(B, maxb)
+    hs = [torch.empty(sbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    ds = [torch.empty(sbytes, dtype=torch.uint8, device="cuda") for _ in range(dev_buffers)]
+    ws = torch.zeros(1 << 21, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    rng = np.random.default_rng(4)
+    inputs, outs, done = [], [], [None, None]
+    for step in range(nsteps):
+        kn = synth.cast_storage(rng.standard_normal((B, H_kv, d), dtype=np.float32), dtype)
+        vn = synth.cast_storage(rng.standard_normal((B, H_kv, d), dtype=np.float32), dtype)
+        q = synth.cast_storage(rng.standard_normal((B, H_q, d), dtype=np.float32), dtype)
+        kd, vd, qd = (storage_to_torch(x, dtype).cuda() for x in (kn, vn, q))
+        out = torch.empty_like(qd)
+        j = step % 2
+        if done[j] is not None:
+            done[j].synchronize()        # host staging buffer j is free again
+        pa.pa_decode_step(gs.pool, seqs, kd, vd, gs.cache.k_cache, gs.cache.v_cache, qd, out,
+                          sc.wl.scale, part, maxb, hs[j], ds[step % dev_buffers], ws)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        done[j] = ev
+        inputs.append((kn, vn, q, kd, vd, qd))
+        outs.append(out)
+    torch.cuda.synchronize()
+    for step in range(nsteps):
+        kn, vn, q = inputs[step][:3]
+        slots, pairs = os_.append(list(seqs), 1)
+        if len(pairs):
+            os_.copy(pairs)
+        os_.write(slots, kn, vn)
+        if step == 0:
+            assert len(pairs) == 1
+        ref = os_.decode(q, list(seqs))
+        H.check_attention(to_f64(outs[step], dtype), ref, dtype, range(B))
+    assert_caches_equal(gs, os_)
+
+
 @pytest.mark.parametrize("part", [0, 64])
 def test_seq_order_is_only_a_schedule(part):
     import torch
