@@ -38,6 +38,14 @@ namespace pa {
 // `part` tokens with NW = kChunkTokens / part (1..8), 8 waves when unsplit.
 constexpr int kChunkTokens = 2048;
 
+// Plain decode of contexts of at least this many partitions runs 6 waves per
+// work-group where the rule above gives 4: a third fewer partial writes in
+// the read stream, and two work-groups still fill a CU's 12 wave slots
+// (8 waves would leave 4 idle).  Measured on 32k-131k contexts with
+// 512-token partitions: 477 -> 457 us; shorter ranges lose more to idle waves
+// in a sequence's last chunk than they gain.
+constexpr int kLongParts = 64;
+
 // Scores more than this many log2 units above the running reference trigger a
 // rescale; weights fed to the PV product are at most 2^kRescaleLog2.
 constexpr float kRescaleLog2 = 8.0f;
@@ -928,8 +936,11 @@ inline int waves_per_group(int part) {
 
 template <typename T, int D, int BS>
 void launch_mfma(const DecodeArgs& a) {
-  switch (waves_per_group(a.part)) {
+  int nw = waves_per_group(a.part);
+  if (nw == 4 && a.cas.ngroups == 0 && a.maxP >= kLongParts) nw = 6;
+  switch (nw) {
     case 8: launch_mfma_nw<T, D, BS, 8>(a); break;
+    case 6: launch_mfma_nw<T, D, BS, 6>(a); break;
     case 4: launch_mfma_nw<T, D, BS, 4>(a); break;
     case 2: launch_mfma_nw<T, D, BS, 2>(a); break;
     default: launch_mfma_nw<T, D, BS, 1>(a); break;

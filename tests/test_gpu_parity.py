@@ -201,6 +201,19 @@ def test_decode_small(dtype, h_q, h_kv, d, bs, part, peaked):
     assert np.all(got[0] == 0)
 
 
+@pytest.mark.parametrize("dtype,bs", [("bf16", 32), ("f16", 16)])
+def test_decode_long_contexts(dtype, bs):
+    """Contexts of 64 or more 512-token partitions run work-groups of six
+    partitions; ragged last chunks, one chunk exactly full, and a short
+    sequence in the same launch."""
+    lens = [32768 + 3072 * 2 + 5, 32768, 3072 * 12, 40961, 100]
+    sc = small_scenario(dtype, 16, 2, 128, bs, seed=9090 + bs, lens=lens)
+    say("long contexts", dtype, bs, lens)
+    _, _, got, ref, rows = run_both(sc, 512)
+    ea, er = H.check_attention(got, ref, dtype, rows)
+    say("  max abs", ea, "max rel", er)
+
+
 def test_decode_is_deterministic_and_placement_invariant():
     import torch
     say("determinism / placement")
