@@ -125,13 +125,13 @@ def cascade_plan(pa, torch, dev, tab_h, len_h, wl, part, flags):
     shared at all)."""
     if not flags or wl.dtype == "f32":
         return None
-    pre, groups, members, mp, mm = pa.pa_cascade_plan(tab_h, len_h, wl.block_size, wl.h_q,
-                                                      wl.h_kv, 512)
+    pre, groups, members, mp, mm, mr = pa.pa_cascade_plan(tab_h, len_h, wl.block_size, wl.h_q,
+                                                          wl.h_kv, 512)
     if len(groups) == 0:
         return None
     put = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     return {"prefix": put(pre), "groups": put(groups.reshape(-1)), "members": put(members),
-            "max_prefix": mp, "max_members": mm, "ngroups": len(groups)}
+            "max_prefix": mp, "max_members": mm, "max_rest": mr, "ngroups": len(groups)}
 
 
 def run_decode(pa, out, q, cache, d_tab, d_len, max_ctx, wl, part, ws, flags, order, plan):
@@ -142,7 +142,8 @@ def run_decode(pa, out, q, cache, d_tab, d_len, max_ctx, wl, part, ws, flags, or
     else:
         pa.pa_decode_cascade(out, q, kc, vc, d_tab, d_len, max_ctx, wl.scale, part,
                              plan["prefix"], plan["groups"], plan["members"], plan["max_prefix"],
-                             plan["max_members"], ws, flags=flags, seq_order=order)
+                             plan["max_members"], plan["max_rest"], ws, flags=flags,
+                             seq_order=order)
 
 
 def unique_kv_bytes(tables, lens, wl):

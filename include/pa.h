@@ -220,7 +220,8 @@ pa_status pa_decode_order(const int32_t* block_tables, int max_blocks_per_seq,
  * cache hits; encyclopedia entry, "como funciona": shared prefixes are mapped,
  * not copied) can have that part attended in one pass for all of them: their
  * queries fill two 16-column matrix-core tiles (32 / G sequences of G query
- * heads each), so one read of each K/V block serves the whole group.
+ * heads each; column c: member c / G, query head c % G), so one read of each
+ * K/V block serves the whole group.
  * The rest of every context runs as in pa_decode, and the split-K reduce
  * merges both parts.  Same result as pa_decode up to floating-point rounding
  * order.
@@ -233,20 +234,24 @@ pa_status pa_decode_order(const int32_t* block_tables, int max_blocks_per_seq,
  * of 32 / G members (none when G > 16).  Outputs: prefix_len_out[num_seqs]
  * (L, or 0 for sequences outside any group), groups_out[num_seqs][3] =
  * {first member, member count, L}, members_out[num_seqs] (sequence indices),
- * *num_groups_out, *max_prefix_out (largest L) and *max_members_out (largest
- * member count).
+ * *num_groups_out, *max_prefix_out (largest L), *max_members_out (largest
+ * member count) and *max_rest_out (largest context_lens[s] - prefix_len[s]).
  *
  * pa_decode_cascade: pa_decode plus that plan in device memory
- * (num_groups == 0 is plain pa_decode) and its two host values; groups of
- * at most 16 / G members run one 16-column tile per load, larger ones two.  fp32 runs the plain path.  The
- * workspace must hold pa_decode_cascade_workspace_size(...) bytes, which is
- * non-zero even for an unsplit decode (the two parts meet in the reduce).
+ * (num_groups == 0 is plain pa_decode) and its three host values; max_rest
+ * must be at least the largest context_lens[s] - prefix_len[s] (the reduce
+ * runs only when that part spans several work-groups' worth of partitions).
+ * Groups of at most 16 / G members run one 16-column tile per load, larger
+ * ones two.  fp32 runs the plain path.  The workspace must hold
+ * pa_decode_cascade_workspace_size(...) bytes, which is non-zero even for an
+ * unsplit decode (the two parts meet in the reduce).
  */
 pa_status pa_cascade_plan(const int32_t* block_tables, int max_blocks_per_seq,
                           const int32_t* context_lens, int num_seqs, int block_size,
                           int num_q_heads, int num_kv_heads, int min_prefix,
                           int32_t* prefix_len_out, int32_t* groups_out, int32_t* members_out,
-                          int* num_groups_out, int* max_prefix_out, int* max_members_out);
+                          int* num_groups_out, int* max_prefix_out, int* max_members_out,
+                          int* max_rest_out);
 size_t pa_decode_cascade_workspace_size(int num_seqs, int num_q_heads, int head_dim,
                                         int max_context_len, int partition_size);
 pa_status pa_decode_cascade(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -256,7 +261,7 @@ pa_status pa_decode_cascade(void* out, const void* q, const void* k_cache, const
                             int head_dim, int block_size, int num_blocks, float scale,
                             int partition_size, const int32_t* prefix_len,
                             const int32_t* groups, const int32_t* members, int num_groups,
-                            int max_prefix, int max_members, void* workspace,
+                            int max_prefix, int max_members, int max_rest, void* workspace,
                             size_t workspace_bytes, int dtype, int flags, void* stream);
 
 /*

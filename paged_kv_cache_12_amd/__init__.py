@@ -39,10 +39,11 @@ SIGNATURES = {
     "pa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                        _i, _vp, _sz, _i, _i, _vp]),
     "pa_decode_order": (_i, [_vp, _i, _vp, _i, _vp]),
-    "pa_cascade_plan": (_i, [_vp, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "pa_cascade_plan": (_i, [_vp, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp]),
     "pa_decode_cascade_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "pa_decode_cascade": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
-                               _f, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _i, _i, _vp]),
+                               _f, _i, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _i, _i, _vp]),
     "pa_swap_blocks": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _vp]),
     "pa_pool_set_host_blocks": (_i, [_vp, _i]),
     "pa_seq_swap_out": (_i, [_vp, _vp, _i, _vp, _i, _vp]),
@@ -282,7 +283,7 @@ def pa_decode_order(block_tables: np.ndarray, context_lens: np.ndarray) -> np.nd
 def pa_cascade_plan(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
                     num_q_heads: int, num_kv_heads: int, min_prefix: int = 512):
     """Host plan of the shared-prefix pass: (prefix_len int32 [B], groups int32
-    [n][3], members int32 [m], max_prefix, max_members)."""
+    [n][3], members int32 [m], max_prefix, max_members, max_rest)."""
     tab = np.ascontiguousarray(block_tables, dtype=np.int32)
     lens = np.ascontiguousarray(context_lens, dtype=np.int32)
     B = lens.size
@@ -291,14 +292,15 @@ def pa_cascade_plan(block_tables: np.ndarray, context_lens: np.ndarray, block_si
     pre = np.zeros(max(1, B), dtype=np.int32)
     groups = np.zeros((max(1, B), 3), dtype=np.int32)
     members = np.zeros(max(1, B), dtype=np.int32)
-    ng, mp, mm = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    ng, mp, mm, mr = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
     _check(lib().pa_cascade_plan(_np_ptr(tab), tab.shape[1], _np_ptr(lens), B, block_size,
                                  num_q_heads, num_kv_heads, min_prefix, _np_ptr(pre),
                                  _np_ptr(groups), _np_ptr(members), ctypes.byref(ng),
-                                 ctypes.byref(mp), ctypes.byref(mm)), "pa_cascade_plan")
+                                 ctypes.byref(mp), ctypes.byref(mm), ctypes.byref(mr)),
+           "pa_cascade_plan")
     g = groups[:ng.value]
     nm = int(g[:, 1].sum()) if ng.value else 0
-    return pre[:B], g, members[:nm], mp.value, mm.value
+    return pre[:B], g, members[:nm], mp.value, mm.value, mr.value
 
 
 def pa_decode_cascade_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int,
@@ -309,8 +311,8 @@ def pa_decode_cascade_workspace_size(num_seqs: int, num_q_heads: int, head_dim: 
 
 def pa_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
                       scale: float, partition_size: int, prefix_len, groups, members,
-                      max_prefix: int, max_members: int, workspace, stream=None, flags: int = 0,
-                      seq_order=None):
+                      max_prefix: int, max_members: int, max_rest: int, workspace, stream=None,
+                      flags: int = 0, seq_order=None):
     """pa_decode with a shared-prefix plan (GPU int32 tensors from pa_cascade_plan)."""
     torch = _torch()
     nb, H_kv, bs, d = cache_geometry(k_cache, v_cache)
@@ -326,7 +328,7 @@ def pa_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens, max_
         None if seq_order is None else _dev_ptr(seq_order, "seq_order"), B, max_context_len, H_q,
         H_kv, d, bs, nb, float(scale), partition_size, _dev_ptr(prefix_len, "prefix_len"),
         _dev_ptr(groups, "groups"), _dev_ptr(members, "members"), ng, max_prefix, max_members,
-        _dev_ptr(workspace, "workspace"), workspace.numel(), torch_dtype_code(q), flags,
+        max_rest, _dev_ptr(workspace, "workspace"), workspace.numel(), torch_dtype_code(q), flags,
         _stream_ptr(stream))
     _check(st, "pa_decode_cascade")
 

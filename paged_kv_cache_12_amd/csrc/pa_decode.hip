@@ -609,22 +609,41 @@ void decode_part_mfma(
     const int64_t row = static_cast<int64_t>(s_col[t]) * H_q + kvh * G + hin[t];
     if constexpr (MODE == kSuffix) {
       if (final_out && slot0 > 0) {
-        // M = max over the prefix partials and this state, weights 2^(m_p - M)
+        // M = max over the prefix partials and this state, weights 2^(m_p - M);
+        // the reads are issued in batches (8 maxima, then two partials at a
+        // time) so that their latencies overlap
         const int64_t base = row * ws_stride;
         float mm = m[t];
-        for (int p = 0; p < slot0; ++p) mm = fmaxf(mm, ws_ml[base + p].x);
+        for (int p0 = 0; p0 < slot0; p0 += 8) {
+          float mx[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) mx[u] = p0 + u < slot0 ? ws_ml[base + p0 + u].x : -INFINITY;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) mm = fmaxf(mm, mx[u]);
+        }
         const float fs = m[t] == -INFINITY ? 0.f : fast_exp2(m[t] - mm);
         lt[t] *= fs;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) o[t][j] *= fs;
-        for (int p = 0; p < slot0; ++p) {
-          const float2 v = ws_ml[base + p];
-          const float f = v.x == -INFINITY ? 0.f : fast_exp2(v.x - mm);
-          lt[t] = fmaf(f, v.y, lt[t]);
-          const float* src = ws_o + (base + p) * D + 4 * g;
+        for (int p0 = 0; p0 < slot0; p0 += 2) {
+          float2 v[2];
+          f32x4 po[2][NJ];
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            o[t][j] += f * *reinterpret_cast<const f32x4*>(src + 16 * j);
+          for (int u = 0; u < 2; ++u) {
+            const int p = p0 + u < slot0 ? p0 + u : p0;
+            v[u] = ws_ml[base + p];
+            const float* src = ws_o + (base + p) * D + 4 * g;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) po[u][j] = *reinterpret_cast<const f32x4*>(src + 16 * j);
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float f =
+                p0 + u >= slot0 || v[u].x == -INFINITY ? 0.f : fast_exp2(v[u].x - mm);
+            lt[t] = fmaf(f, v[u].y, lt[t]);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) o[t][j] += f * po[u][j];
+          }
         }
       }
     }
@@ -873,6 +892,7 @@ struct DecodeArgs {
   Cascade cas;           // ngroups > 0: prefix pass + suffix pass
   int max_prefix;        // longest group prefix
   int max_members;       // largest group
+  int max_rest;          // longest context part outside a group's prefix
   NewKV nkv;             // the step's appended K/V, or nulls
 };
 
@@ -921,7 +941,7 @@ void launch_mfma_nw(const DecodeArgs& a) {
   else
     launch_part<T, D, BS, NWP, false, kPrefix>(a, cp, stride, a.cas.ngroups);
   launch_part<T, D, BS, NW, true, kSuffix>(a, maxC, stride, a.B);
-  if (maxC > 1)  // some suffix may take several chunks
+  if (host_chunks(a.max_rest, a.part, NW) > 1)  // some rest takes several chunks
     hipLaunchKernelGGL((decode_reduce<T, D, NW>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0,
                        a.st, static_cast<T*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens,
                        a.H_q, a.part, stride, a.cas.prefix_len);
@@ -1033,7 +1053,8 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   if (cascade && (!plan->prefix_len || !plan->groups || !plan->members || plan->ngroups < 0 ||
                   plan->max_prefix < 0 || plan->max_prefix > max_context_len ||
                   plan->max_members < 1 ||
-                  plan->max_members * (num_q_heads / num_kv_heads) > 32))
+                  plan->max_members * (num_q_heads / num_kv_heads) > 32 ||
+                  plan->max_rest < 0 || plan->max_rest > max_context_len))
     return PA_ERR_INVALID;
   const size_t need =
       cascade ? pa_decode_cascade_workspace_size(num_seqs, num_q_heads, head_dim,
@@ -1065,6 +1086,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   a.cas = Cascade{nullptr, nullptr, nullptr, 0};
   a.max_prefix = 0;
   a.max_members = 0;
+  a.max_rest = 0;
   a.nkv = NewKV{nullptr, nullptr};
   if (nkv && nkv->k && nkv->v && dtype != PA_F32) {
     if (!aligned16(nkv->k) || !aligned16(nkv->v)) return PA_ERR_INVALID;
@@ -1075,6 +1097,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
     a.cas = Cascade{plan->prefix_len, plan->groups, plan->members, plan->ngroups};
     a.max_prefix = plan->max_prefix;
     a.max_members = plan->max_members;
+    a.max_rest = plan->max_rest;
     slots = host_chunks(max_context_len, a.part, std::min(waves_per_group(a.part), kPrefixWaves)) + 1;
   }
   if (need > 0) {
@@ -1125,10 +1148,11 @@ PA_EXPORT pa_status pa_decode_cascade(void* out, const void* q, const void* k_ca
                                       int partition_size, const int32_t* prefix_len,
                                       const int32_t* groups, const int32_t* members,
                                       int num_groups, int max_prefix, int max_members,
-                                      void* workspace, size_t workspace_bytes, int dtype,
-                                      int flags, void* stream) {
+                                      int max_rest, void* workspace, size_t workspace_bytes,
+                                      int dtype, int flags, void* stream) {
   if (num_groups < 0) return PA_ERR_INVALID;
-  const CascadePlan plan{prefix_len, groups, members, num_groups, max_prefix, max_members};
+  const CascadePlan plan{prefix_len, groups, members, num_groups, max_prefix, max_members,
+                         max_rest};
   return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, flags,

@@ -36,7 +36,8 @@ inline pa_status launch_status() {
 // Shared-prefix (cascade) plan, device arrays: prefix_len[num_seqs],
 // groups[ngroups][3] = {first member, member count, prefix tokens},
 // members[] = sequence indices; max_prefix = largest prefix, max_members =
-// largest group (host values).
+// largest group, max_rest = longest context part outside its group's prefix
+// (host values).
 struct CascadePlan {
   const int32_t* prefix_len;
   const int32_t* groups;
@@ -44,6 +45,7 @@ struct CascadePlan {
   int ngroups;
   int max_prefix;
   int max_members;
+  int max_rest;
 };
 
 // The step's appended K/V ([num_seqs][H_kv][head_dim], device; fp16 / bf16),

@@ -511,21 +511,33 @@ PA_EXPORT pa_status pa_cascade_plan(const int32_t* block_tables, int max_blocks_
                                     int num_q_heads, int num_kv_heads, int min_prefix,
                                     int32_t* prefix_len_out, int32_t* groups_out,
                                     int32_t* members_out, int* num_groups_out,
-                                    int* max_prefix_out, int* max_members_out) {
+                                    int* max_prefix_out, int* max_members_out,
+                                    int* max_rest_out) {
   if (num_seqs < 0 || max_blocks_per_seq < 0 || block_size <= 0 || num_q_heads <= 0 ||
       num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || !num_groups_out ||
-      !max_prefix_out || !max_members_out)
+      !max_prefix_out || !max_members_out || !max_rest_out)
     return PA_ERR_INVALID;
   *num_groups_out = 0;
   *max_prefix_out = 0;
   *max_members_out = 0;
+  *max_rest_out = 0;
   if (num_seqs == 0) return PA_OK;
   if (!block_tables || !context_lens || !prefix_len_out || !groups_out || !members_out)
     return PA_ERR_INVALID;
   for (int s = 0; s < num_seqs; ++s) prefix_len_out[s] = 0;
+  // the longest context outside any group's prefix (updated below)
+  auto rest = [&]() {
+    int r = 0;
+    for (int s = 0; s < num_seqs; ++s)
+      r = std::max(r, std::max(context_lens[s], 0) - prefix_len_out[s]);
+    *max_rest_out = r;
+  };
   const int G = num_q_heads / num_kv_heads;
   const int cap = G <= 16 ? 32 / G : 0;  // sequences per 2 x 16 MFMA columns
-  if (cap < 2 || max_blocks_per_seq == 0) return PA_OK;
+  if (max_blocks_per_seq == 0 || cap == 0) {
+    rest();
+    return PA_OK;
+  }
   // families: sequences whose tables start with the same physical block, in
   // order of first appearance, members in index order
   std::unordered_map<int32_t, int32_t> fam_of;
@@ -569,6 +581,7 @@ PA_EXPORT pa_status pa_cascade_plan(const int32_t* block_tables, int max_blocks_
     *max_prefix_out = std::max(*max_prefix_out, L);
   }
   *num_groups_out = ng;
+  rest();
   return PA_OK;
 }
 
@@ -597,4 +610,4 @@ PA_EXPORT const char* pa_status_str(int status) {
   }
 }
 
-PA_EXPORT int pa_abi_version(void) { return 3; }
+PA_EXPORT int pa_abi_version(void) { return 4; }

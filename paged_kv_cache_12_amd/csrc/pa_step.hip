@@ -143,7 +143,7 @@ pa_status launch_step(pa_pool* pool, const StepDev& a, const int64_t* seqs, int 
   // when the workspace has room for the cascade's partials
   CascadePlan plan{reinterpret_cast<const int32_t*>(d + L.prefix),
                    reinterpret_cast<const int32_t*>(d + L.groups),
-                   reinterpret_cast<const int32_t*>(d + L.members), 0, 0, 0};
+                   reinterpret_cast<const int32_t*>(d + L.members), 0, 0, 0, 0};
   if (flags && a.dtype != PA_F32 &&
       pa_decode_cascade_workspace_size(n, a.num_q_heads, a.head_dim, max_ctx,
                                        a.partition_size) <= a.workspace_bytes &&
@@ -153,7 +153,7 @@ pa_status launch_step(pa_pool* pool, const StepDev& a, const int64_t* seqs, int 
                          reinterpret_cast<int32_t*>(h + L.prefix),
                          reinterpret_cast<int32_t*>(h + L.groups),
                          reinterpret_cast<int32_t*>(h + L.members), &plan.ngroups,
-                         &plan.max_prefix, &plan.max_members);
+                         &plan.max_prefix, &plan.max_members, &plan.max_rest);
     if (st != PA_OK) return st;
   }
 

@@ -49,7 +49,7 @@ def test_status_strings(L):
     assert pa.status_str(0) == "ok"
     assert pa.status_str(3) == "not enough free blocks"
     assert pa.status_str(99) == "unknown status"
-    assert L.pa_abi_version() == 3
+    assert L.pa_abi_version() == 4
 
 
 def test_kv_bytes_per_token_matches_closed_form(L):
@@ -324,8 +324,9 @@ def _plan_by_definition(tab, lens, bs, G, min_prefix):
     pre = [0] * B
     groups, members = [], []
     cap = 32 // G if G <= 16 else 0
+    rest = lambda: max([max(int(n), 0) - p for n, p in zip(lens, pre)] + [0])
     if cap < 2:
-        return pre, groups, members, 0, 0
+        return pre, groups, members, 0, 0, rest()
     fams, order = {}, []
     for s in range(B):
         if lens[s] <= 0 or tab[s][0] < 0:
@@ -355,7 +356,7 @@ def _plan_by_definition(tab, lens, bs, G, min_prefix):
             for s in part:
                 pre[s] = L
         mp = max(mp, L)
-    return pre, groups, members, mp, mm
+    return pre, groups, members, mp, mm, rest()
 
 
 @pytest.mark.parametrize("seed,G", [(0, 4), (1, 1), (2, 8), (3, 16), (4, 2)])
@@ -373,13 +374,13 @@ def test_cascade_plan_matches_its_definition(L, seed, G):
         tab[s, :nb] = row
     for mp_min in (0, 64, 512):
         got = pa.pa_cascade_plan(tab, lens, bs, 8 * G, 8, mp_min)
-        pre, groups, members, mp, mm = _plan_by_definition(tab, lens, bs, G, mp_min)
+        pre, groups, members, mp, mm, mr = _plan_by_definition(tab, lens, bs, G, mp_min)
         assert got[0].tolist() == pre
         assert got[1].tolist() == groups
         assert got[2].tolist() == members
-        assert got[3] == mp and got[4] == mm
+        assert got[3] == mp and got[4] == mm and got[5] == mr
     # every member of a group holds the same blocks for its prefix
-    pre, groups, members, _, _ = pa.pa_cascade_plan(tab, lens, bs, 8 * G, 8, 0)
+    pre, groups, members, _, _, _ = pa.pa_cascade_plan(tab, lens, bs, 8 * G, 8, 0)
     for first, cnt, Lp in groups.tolist():
         rows = [tab[m, :-(-Lp // bs)] for m in members[first:first + cnt]]
         assert all((r == rows[0]).all() for r in rows) and all(lens[m] >= Lp for m in members[first:first + cnt])

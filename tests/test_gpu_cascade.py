@@ -32,6 +32,8 @@ def _gpu():
 def _workload(name):
     if name == "prefix_g4":
         return synth.WORKLOADS["shared_prefix_bf16"], dict(batch=18, ctx_hi=300)
+    if name == "prefix_g4_wide":    # 40 sharers: column groups of 32 and 8 members
+        return synth.WORKLOADS["shared_prefix_bf16"], dict(batch=40, ctx_hi=120)
     if name == "cow_g1":
         return synth.WORKLOADS["opt13b_sampling_cow_fp16"], dict(batch=16, ctx_hi=150)
     if name == "prefix_g8_bs32":
@@ -47,6 +49,7 @@ def _workload(name):
 
 
 @pytest.mark.parametrize("name,part", [("prefix_g4", 512), ("prefix_g4", 0), ("prefix_g4", 64),
+                                       ("prefix_g4_wide", 512), ("prefix_g4_wide", 32),
                                        ("cow_g1", 512), ("cow_g1", 0), ("prefix_g8_bs32", 96),
                                        ("prefix_g4_f16_d64", 256), ("prefix_g4_f16_d64", 0)])
 def test_cascade_decode_matches_oracle(name, part):
@@ -62,8 +65,8 @@ def test_cascade_decode_matches_oracle(name, part):
     H.execute(sc, os_)
     seqs = sc.decode_seqs
     tab, lens = gs.cache.tables(seqs)
-    pre, groups, members, mp, mm = pa.pa_cascade_plan(tab, lens, wl.block_size, wl.h_q, wl.h_kv,
-                                                      64)
+    pre, groups, members, mp, mm, mr = pa.pa_cascade_plan(tab, lens, wl.block_size, wl.h_q,
+                                                          wl.h_kv, 64)
     assert len(groups) > 0 and mp > 0
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q = storage_to_torch(sc.q, wl.dtype).cuda()
@@ -74,8 +77,8 @@ def test_cascade_decode_matches_oracle(name, part):
     order = dev(pa.pa_decode_order(tab, lens))
     out = torch.empty_like(q)
     pa.pa_decode_cascade(out, q, gs.cache.k_cache, gs.cache.v_cache, dev(tab), dev(lens), max_ctx,
-                         wl.scale, part, dev(pre), dev(groups.reshape(-1)), dev(members), mp, mm, ws,
-                         flags=pa.PA_DECODE_SHARED_KV, seq_order=order)
+                         wl.scale, part, dev(pre), dev(groups.reshape(-1)), dev(members), mp, mm, mr,
+                         ws, flags=pa.PA_DECODE_SHARED_KV, seq_order=order)
     plain = torch.empty_like(q)
     ws2 = torch.zeros(max(256, pa.pa_decode_workspace_size(len(seqs), wl.h_q, wl.head_dim,
                                                            max_ctx, part)),
@@ -92,7 +95,8 @@ def test_cascade_decode_matches_oracle(name, part):
     again = torch.empty_like(q)
     pa.pa_decode_cascade(again, q, gs.cache.k_cache, gs.cache.v_cache, dev(tab), dev(lens),
                          max_ctx, wl.scale, part, dev(pre), dev(groups.reshape(-1)),
-                         dev(members), mp, mm, ws, flags=pa.PA_DECODE_SHARED_KV, seq_order=order)
+                         dev(members), mp, mm, mr, ws, flags=pa.PA_DECODE_SHARED_KV,
+                         seq_order=order)
     torch.cuda.synchronize()
     assert torch.equal(again.view(torch.int16), out.view(torch.int16))
 
@@ -115,7 +119,7 @@ def test_cascade_with_no_groups_is_plain_decode():
     a, b = torch.empty_like(q), torch.empty_like(q)
     empty = torch.zeros(0, dtype=torch.int32, device="cuda")
     pa.pa_decode_cascade(a, q, gs.cache.k_cache, gs.cache.v_cache, dev(tab), dev(lens), mc,
-                         wl.scale, 512, dev(np.zeros(B, np.int32)), empty, empty, 0, 0, ws)
+                         wl.scale, 512, dev(np.zeros(B, np.int32)), empty, empty, 0, 0, mc, ws)
     pa.pa_decode(b, q, gs.cache.k_cache, gs.cache.v_cache, dev(tab), dev(lens), mc, wl.scale,
                  512, workspace=ws)
     torch.cuda.synchronize()
@@ -144,7 +148,7 @@ def test_decode_step_uses_the_cascade_for_long_shared_prefixes(dtype, part):
     B = len(seqs)
     maxb = 64
     tab, ln = os_.tables(list(seqs))
-    pre, groups, members, mp, _ = pa.pa_cascade_plan(tab, ln + 1, bs, H_q, H_kv, 512)
+    pre, groups, members, mp, _, _ = pa.pa_cascade_plan(tab, ln + 1, bs, H_q, H_kv, 512)
     assert len(groups) == 2 and mp == 896          # the step's plan: two families
     sbytes = pa.pa_decode_step_staging_size(B, maxb)
     hs = [torch.empty(sbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
