@@ -206,17 +206,21 @@ __device__ __forceinline__ void load_group(GroupTiles<T, D>& G, TableWindow& w,
   constexpr int NC = D / 32, NJ = D / 16, BPT = 32 / BS;
   const int lb0 = tg / BS;
   if (lb0 + BPT - 1 >= w.lb_base + 64) fill_window(w, bt, lb0, nb_valid, num_blocks, lane);
-  int pb[BPT];
+  // block offsets are wave-uniform (scalar multiplies); each lane then only
+  // selects the one of its block
+  int64_t boff[BPT];
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) pb[j] = __builtin_amdgcn_readlane(w.ids, lb0 + j - w.lb_base);
+  for (int j = 0; j < BPT; ++j)
+    boff[j] = static_cast<int64_t>(__builtin_amdgcn_readlane(w.ids, lb0 + j - w.lb_base)) *
+              blk_stride;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const T* base = kh + pb[kblk[h]] * blk_stride + krow[h] * 8;
+    const T* base = kh + boff[kblk[h]] + krow[h] * 8;
 #pragma unroll
     for (int k = 0; k < NC; ++k)
       G.k[h][k] = load16<v8, NT>(base + (4 * k + g) * (BS * 8));
   }
-  const T* base = vh + pb[vblk] * blk_stride + vslab * (D * 8) + c * 8;
+  const T* base = vh + boff[vblk] + vslab * (D * 8) + c * 8;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) G.v[j] = load16<v8, NT>(base + 16 * j * 8);
 }
@@ -417,7 +421,10 @@ void decode_part_mfma(
   constexpr int NJ = D / 16;    // PV output chunks of 16 dims
   constexpr int TILE = BS * D;  // elements per (block, head) tile
 
-  const int wave = threadIdx.x >> 6;
+  // the wave index through readfirstlane: the compiler then keeps every
+  // per-wave value (token range, loop counter, block offsets) in scalar
+  // registers and runs the loop on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;  // MFMA row/column index within a lane group
   const int g = lane >> 4;  // lane group
@@ -936,10 +943,22 @@ void launch_mfma_nw(const DecodeArgs& a) {
   constexpr int NWP = PrefixNW<NW>::value;
   const int stride = host_chunks(a.max_tokens, a.part, NWP) + 1;
   const int cp = host_chunks(a.max_prefix, a.part, NWP);
-  if (a.max_members * a.G > 16)
-    launch_part<T, D, BS, NWP, false, kPrefix2>(a, cp, stride, a.cas.ngroups);
-  else
-    launch_part<T, D, BS, NWP, false, kPrefix>(a, cp, stride, a.cas.ngroups);
+  // A family wider than one column group (32 / G members) spans several
+  // groups that re-read its blocks: cached loads, XCD-aware order.  When the
+  // largest group is smaller than that, every group is a whole family and
+  // each prefix block is read once: streaming loads, as in the plain pass.
+  const bool reread = a.max_members >= 32 / a.G;
+  if (a.max_members * a.G > 16) {
+    if (reread)
+      launch_part<T, D, BS, NWP, false, kPrefix2>(a, cp, stride, a.cas.ngroups);
+    else
+      launch_part<T, D, BS, NWP, true, kPrefix2>(a, cp, stride, a.cas.ngroups);
+  } else {
+    if (reread)
+      launch_part<T, D, BS, NWP, false, kPrefix>(a, cp, stride, a.cas.ngroups);
+    else
+      launch_part<T, D, BS, NWP, true, kPrefix>(a, cp, stride, a.cas.ngroups);
+  }
   launch_part<T, D, BS, NW, true, kSuffix>(a, maxC, stride, a.B);
   if (host_chunks(a.max_rest, a.part, NW) > 1)  // some rest takes several chunks
     hipLaunchKernelGGL((decode_reduce<T, D, NW>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0,
