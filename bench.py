@@ -22,6 +22,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -34,7 +35,10 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "llama3_8b_gqa_bf16"
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_12_amd", "csrc", "pa_decode.hip")
+# the decode kernels' code: their source and the headers it includes
+DECODE_SRC = [os.path.join(ROOT, "paged_kv_cache_12_amd", "csrc", f)
+              for f in ("pa_decode.hip", "pa_internal.h", "pa_kv_store.h")] + \
+    [os.path.join(ROOT, "include", "pa.h")]
 
 
 def parse():
@@ -81,7 +85,16 @@ def calibrate():
 
 
 def source_hash() -> str:
-    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the decode kernels' code with comments and whitespace removed:
+    the counters in profiles/ stay attached to the code they were taken on,
+    and an edit of comments alone does not detach them."""
+    h = hashlib.sha256()
+    for path in DECODE_SRC:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def fill_cache(sc, cache, dev):

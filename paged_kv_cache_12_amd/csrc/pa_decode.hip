@@ -3,10 +3,15 @@
 // one block at a time, output accumulated against the same block's values,
 // blocks anywhere in memory) and "o que isso custou" (the fused kernel).
 //
-// Work unit: one wavefront per (partition of the context, KV head, sequence).
-// A partition is a run of `part` tokens (whole context when part == 0); its
-// result is either the final output (one partition) or a partial (running max
-// m in log2 units, sum l, unnormalised output o) merged by decode_reduce.
+// Work unit: a work-group of NW wavefronts per (chunk of NW partitions, KV
+// head [x head group], sequence).  Each wave runs one partition, a run of
+// `part` tokens (a range that fits one chunk, always the case when part == 0,
+// is instead split evenly over the waves) with its own running state (max m
+// in log2 units, sum l, unnormalised output o); the waves merge in LDS and
+// the work-group writes the final output, or one partial per chunk that
+// decode_reduce merges.  With an appended token (the decode step), the wave
+// that ends each context also performs its block write.  The shared-prefix
+// (cascade) modes are described at decode_part_mfma's modes below.
 //
 // fp16 / bf16 path (decode_part_mfma): the G query heads that share a KV head
 // (GQA) are the N = 16 columns of 16x16x32 MFMAs, so one KV read serves the
