@@ -345,9 +345,10 @@ def test_decode_step_matches_oracle(dtype, part):
     assert_caches_equal(gs, os_)
 
 
-@pytest.mark.parametrize("dtype,part,dev_buffers", [("bf16", 0, 2), ("f16", 64, 1),
-                                                    ("bf16", 32, 2), ("f32", 0, 2)])
-def test_decode_steps_back_to_back(dtype, part, dev_buffers):
+@pytest.mark.parametrize("dtype,part,dev_buffers,bs,d", [
+    ("bf16", 0, 2, 16, 128), ("f16", 64, 1, 16, 128), ("bf16", 32, 2, 16, 128),
+    ("f32", 0, 2, 16, 64), ("bf16", 64, 2, 32, 64), ("f16", 0, 1, 32, 128)])
+def test_decode_steps_back_to_back(dtype, part, dev_buffers, bs, d):
     """Steps enqueued without waiting for the GPU in between: each step's
     staging copy runs on the library's side stream while the previous step's
     kernels may still run.  Every step's output and the final caches must
@@ -355,9 +356,9 @@ def test_decode_steps_back_to_back(dtype, part, dev_buffers):
     import torch
     import paged_kv_cache_12_amd as pa
     from paged_kv_cache_12_amd.manager import storage_to_torch
-    say("decode_steps_back_to_back", dtype, part, dev_buffers)
-    H_q, H_kv, d, bs = 8, 2, 64 if dtype == "f32" else 128, 16
-    lens = [1, 15, 16, 33, 200, 31]
+    say("decode_steps_back_to_back", dtype, part, dev_buffers, bs, d)
+    H_q, H_kv = 8, 2
+    lens = [1, 15, 16, 33, 200, 31] if bs == 16 else [1, 31, 32, 33, 200, 63]
     sc = small_scenario(dtype, H_q, H_kv, d, bs, seed=6262 + part, lens=lens)
     sc.ops += [("fork", 3, 6)]        # a shared, partly filled last block
     sc.decode_seqs = [0, 1, 2, 3, 4, 5, 6]
@@ -368,7 +369,7 @@ def test_decode_steps_back_to_back(dtype, part, dev_buffers):
     H.execute(sc, os_)
     seqs = np.array(sc.decode_seqs, dtype=np.int64)
     B = len(seqs)
-    maxb = 32
+    maxb = 512 // bs
     nsteps = 12
     sbytes = pa.pa_decode_step_staging_size(B, maxb)
     hs = [torch.empty(sbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
