@@ -214,6 +214,21 @@ def test_decode_long_contexts(dtype, bs):
     say("  max abs", ea, "max rel", er)
 
 
+@pytest.mark.parametrize("dtype,part", [("bf16", 0), ("f16", 32), ("f32", 32)])
+def test_decode_many_short_sequences(dtype, part):
+    """A large batch of short contexts (0 .. 40 tokens): thousands of
+    work-groups, most of them a single partial group, many empty."""
+    lens = np.random.default_rng(42).integers(0, 41, 3000).tolist()
+    d = 64 if dtype == "f32" else 128
+    sc = small_scenario(dtype, 8, 2, d, 16, seed=4242, lens=lens)
+    say("many short sequences", dtype, part, len(lens))
+    gs, os_, got, ref, rows = run_both(sc, part)
+    ea, er = H.check_attention(got, ref, dtype, rows)
+    zero = [s for s, n in enumerate(lens) if n == 0]
+    assert zero and all(np.all(got[s] == 0) for s in zero)
+    say("  max abs", ea, "max rel", er)
+
+
 def test_decode_is_deterministic_and_placement_invariant():
     import torch
     say("determinism / placement")
