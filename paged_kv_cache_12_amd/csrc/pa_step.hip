@@ -91,6 +91,7 @@ pa_status check_dev(const StepDev& a, int n) {
   if (elem_bytes(a.dtype) == 0 || !supported_head_dim(a.head_dim) ||
       !supported_block_size(a.block_size))
     return PA_ERR_UNSUPPORTED;
+  if (n > 65535 || a.num_q_heads > 65535) return PA_ERR_INVALID;  // the decode's grid limits
   if (a.num_q_heads <= 0 || a.num_kv_heads <= 0 || a.num_q_heads % a.num_kv_heads != 0 ||
       a.num_blocks <= 0 || a.partition_size < 0 || a.partition_size % 32 != 0 ||
       !std::isfinite(a.scale))

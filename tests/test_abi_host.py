@@ -263,11 +263,19 @@ def test_decode_step_rejects_before_touching_the_pool(L):
     assert _step(L, pool, [0, 1], part=32) == INV         # needs a workspace, none given
     assert _step(L, pool, [0, 7]) == pa.PA_ERR_UNKNOWN_SEQ
     assert _step(L, pool, [0, 0]) == INV                  # duplicate ids (append rejects)
+    assert _step(L, pool, [0, 1], H_q=70000, H_kv=2) == INV   # beyond the decode's grid
     full = pa.Pool(2, 16, [0, 1])
     full.create(0)
     full.append(0, 32)
     assert _step(L, full, [0]) == pa.PA_ERR_NO_BLOCKS
     assert (pool.free_list().tolist(), pool.stats()) == before
+    # more sequences than the decode's grid takes: rejected before any append
+    big = pa.Pool(65536, 16, None)
+    for s in range(65536):
+        big.create(s)
+    bstats = big.stats()
+    assert _step(L, big, np.arange(65536), maxb=1, sbytes=1 << 30) == INV
+    assert big.stats() == bstats
     # slots, pairs, lengths, order, prefix lengths, groups, members, tables
     assert pa.pa_decode_step_staging_size(64, 257) == 512 + 512 + 256 + 256 + 256 + 768 + 256 + (64 * 257 * 4 + 255) // 256 * 256
 
