@@ -97,6 +97,31 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def read_ceiling(pa, torch, dev, stream, runs: int = 10):
+    """The decode's access pattern without the math: pa_read_probe over 4 GiB
+    of random 4 KiB tiles (each read once per run), timed with HIP events on
+    the launch stream; GB/s with non-temporal and with plain 16-byte loads."""
+    tile, total = 4096, 4 << 30
+    buf = torch.empty(total, dtype=torch.uint8, device=dev)
+    g = torch.Generator().manual_seed(2024)
+    order = torch.randperm(total // tile, generator=g).to(torch.int32).to(dev)
+    partials = torch.empty(16 * pa.pa_read_probe_partials(), dtype=torch.uint8, device=dev)
+    res = {}
+    for nt in (True, False):
+        for _ in range(2):
+            pa.pa_read_probe(buf, tile, order, partials, nt)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(runs):
+            pa.pa_read_probe(buf, tile, order, partials, nt)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / runs
+        res["nontemporal_GBps" if nt else "plain_GBps"] = round(total / (ms * 1e-3) / 1e9, 1)
+    del buf, order, partials
+    return res
+
+
 def fill_cache(sc, cache, dev):
     """Run the workload's op script through the product path (C++ pool +
     pa_copy_blocks + pa_write_kv)."""
@@ -714,6 +739,10 @@ def main():
                 "bytes_read_plus_written": c_bytes,
                 "GBps": round(c_bytes / (c_ms * 1e-3) / 1e9, 1)}
     del copies
+    # context: the same access pattern without the math
+    ceiling = read_ceiling(pa, torch, dev, stream)
+    ceiling["pattern"] = "random 4 KiB tiles of 4 GiB, 16-byte loads, each tile once (pa_read_probe)"
+    ceiling["decode_frac_of_nontemporal"] = round(unique_rate / ceiling["nontemporal_GBps"], 4)
 
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
@@ -765,6 +794,7 @@ def main():
                      "bytes_per_launch": round(unique),
                      "logical_bytes_per_launch": round(kv_dec),
                      "logical_achieved": round(achieved, 1)},
+        "read_ceiling": ceiling,
     }
     if cpu is not None:
         res["cpu_baseline"] = cpu

@@ -126,6 +126,28 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
                          int dtype, void* stream);
 
 /*
+ * pa_read_probe — a measurement helper, not part of the decode: the read rate
+ * the decode's access pattern can reach on this device.  Reads num_tiles
+ * tiles of tile_bytes bytes of buf in the order tile_order gives (read i is
+ * tile tile_order[i]; entries outside [0, num_tiles) are skipped, so a
+ * permutation reads every tile once), with 16-byte loads, non-temporal when
+ * nontemporal != 0 as the decode's K/V loads are.  Each of the
+ * pa_read_probe_partials() waves of the fixed grid writes the XOR of the
+ * 16-byte vectors it read to partials[wave], so the XOR of all partials is the
+ * XOR of every tile read.
+ *   buf         device memory, num_tiles * tile_bytes bytes, 16-byte aligned
+ *   tile_order  device int32 [num_tiles]
+ *   partials    device, pa_read_probe_partials() x 16 bytes, 16-byte aligned
+ * PA_ERR_INVALID for tile_bytes not a positive multiple of 1024, a negative or
+ * larger than INT32_MAX tile count, or a null / misaligned pointer.
+ * Asynchronous on `stream`.
+ */
+int pa_read_probe_partials(void);
+pa_status pa_read_probe(const void* buf, int64_t num_tiles, int tile_bytes,
+                        const int32_t* tile_order, int nontemporal, void* partials,
+                        void* stream);
+
+/*
  * pa_swap_blocks — whole-block copies between two caches of the same
  * geometry, for swapping sequences out to host memory and back (encyclopedia
  * entry, "a ideia": the cache can be swapped to CPU RAM; "como funciona": a

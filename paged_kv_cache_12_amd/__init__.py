@@ -45,6 +45,8 @@ SIGNATURES = {
     "pa_decode_cascade": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                _f, _i, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _i, _i, _vp]),
     "pa_swap_blocks": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _vp]),
+    "pa_read_probe_partials": (_i, []),
+    "pa_read_probe": (_i, [_vp, _i64, _i, _vp, _i, _vp, _vp]),
     "pa_pool_set_host_blocks": (_i, [_vp, _i]),
     "pa_seq_swap_out": (_i, [_vp, _vp, _i, _vp, _i, _vp]),
     "pa_seq_swap_in": (_i, [_vp, _vp, _i, _vp, _i, _vp]),
@@ -222,6 +224,27 @@ def pa_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None):
                               _any_ptr(pairs, "pairs"), P, H, d, bs, torch_dtype_code(src_k),
                               _stream_ptr(stream))
     _check(st, "pa_swap_blocks")
+
+
+def pa_read_probe_partials() -> int:
+    return int(lib().pa_read_probe_partials())
+
+
+def pa_read_probe(buf, tile_bytes: int, tile_order, partials, nontemporal: bool = True,
+                  stream=None):
+    """Read-rate probe (measurement helper): reads buf (GPU uint8 tensor) as
+    tiles of tile_bytes in tile_order (GPU int32 tensor); partials (GPU
+    tensor of pa_read_probe_partials() x 16 bytes) receives each wave's XOR."""
+    torch = _torch()
+    if tile_order.dtype != torch.int32:
+        raise TypeError("tile_order must be int32")
+    num_tiles = buf.numel() * buf.element_size() // tile_bytes
+    if partials.numel() * partials.element_size() < 16 * pa_read_probe_partials():
+        raise ValueError("partials too small")
+    st = lib().pa_read_probe(_dev_ptr(buf, "buf"), num_tiles, tile_bytes,
+                             _dev_ptr(tile_order, "tile_order"), int(bool(nontemporal)),
+                             _dev_ptr(partials, "partials"), _stream_ptr(stream))
+    _check(st, "pa_read_probe")
 
 
 def pa_decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int,

@@ -68,6 +68,57 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(
     to[i] = from[i];
 }
 
+// Read-rate probe (a measurement helper, not part of the decode): each wave
+// reads whole tiles, four at a time (tiles wave, wave + nwaves, ... of the
+// order array), with 16-byte loads, non-temporal when NT, and XORs what it
+// read; the wave's XOR lands in partials[wave].  The grid is fixed at
+// kProbeGroups work-groups of 4 waves.
+constexpr int kProbeGroups = 2048;
+constexpr int kProbeWaves = kProbeGroups * 4;
+
+template <bool NT>
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ buf,
+                                                         int64_t num_tiles, int tile_vecs,
+                                                         const int32_t* __restrict__ order,
+                                                         u32x4* __restrict__ partials) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = __builtin_amdgcn_readfirstlane(
+      static_cast<int>((static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6));
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int64_t i = wave; i < num_tiles; i += 4 * nwaves) {
+    int64_t base[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t k = i + u * nwaves;
+      const int32_t t = k < num_tiles ? order[k] : -1;
+      base[u] = t >= 0 && t < num_tiles ? static_cast<int64_t>(t) * tile_vecs : -1;
+    }
+#pragma unroll 4
+    for (int v = lane; v < tile_vecs; v += 64) {
+      u32x4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[u] = u32x4{0u, 0u, 0u, 0u};
+        if (base[u] >= 0) {
+          if constexpr (NT)
+            x[u] = __builtin_nontemporal_load(buf + base[u] + v);
+          else
+            x[u] = buf[base[u] + v];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc ^= x[u];
+    }
+  }
+#pragma unroll
+  for (int mask = 32; mask >= 1; mask >>= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc[e] ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc[e]), mask, 64));
+  if (lane == 0) partials[wave] = acc;
+}
+
 // Device-side address of a cache or pair array: device memory as is, pinned
 // host memory through its device mapping; nullptr for anything else.
 void* device_view(const void* p) {
@@ -182,5 +233,26 @@ PA_EXPORT pa_status pa_swap_blocks(const void* src_k, const void* src_v, int src
                      static_cast<const u32x4*>(sk), static_cast<const u32x4*>(sv),
                      static_cast<u32x4*>(dk), static_cast<u32x4*>(dv),
                      static_cast<const int32_t*>(pp), src_blocks, dst_blocks, vecs);
+  return launch_status();
+}
+
+PA_EXPORT int pa_read_probe_partials(void) { return kProbeWaves; }
+
+PA_EXPORT pa_status pa_read_probe(const void* buf, int64_t num_tiles, int tile_bytes,
+                                  const int32_t* tile_order, int nontemporal, void* partials,
+                                  void* stream) {
+  if (num_tiles < 0 || num_tiles > INT32_MAX || tile_bytes <= 0 || tile_bytes % 1024 != 0)
+    return PA_ERR_INVALID;
+  if (!partials || !aligned16(partials)) return PA_ERR_INVALID;
+  if (num_tiles > 0 && (!buf || !tile_order || !aligned16(buf))) return PA_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (nontemporal)
+    hipLaunchKernelGGL(read_probe_kernel<true>, dim3(kProbeGroups), dim3(256), 0, st,
+                       static_cast<const u32x4*>(buf), num_tiles, tile_bytes / 16, tile_order,
+                       static_cast<u32x4*>(partials));
+  else
+    hipLaunchKernelGGL(read_probe_kernel<false>, dim3(kProbeGroups), dim3(256), 0, st,
+                       static_cast<const u32x4*>(buf), num_tiles, tile_bytes / 16, tile_order,
+                       static_cast<u32x4*>(partials));
   return launch_status();
 }

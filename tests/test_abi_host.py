@@ -33,7 +33,7 @@ def L():
 
 def test_library_exports_exactly_the_header_functions(L):
     declared = header_functions()
-    assert len(declared) == 39
+    assert len(declared) == 41
     for name in declared:
         assert hasattr(L, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
@@ -101,6 +101,20 @@ def test_decode_validation(L):
     assert _decode(L, B=-1) == INV
     assert _decode(L, H_kv=0) == INV
     assert _decode(L, flags=2) == INV                  # unknown flag
+
+
+def test_read_probe_validation(L):
+    INV = pa.PA_ERR_INVALID
+    P = L.pa_read_probe
+    assert L.pa_read_probe_partials() == 8192
+    assert P(16, 4, 1000, 16, 1, 16, None) == INV           # tile size not a multiple of 1 KiB
+    assert P(16, 4, 0, 16, 1, 16, None) == INV
+    assert P(16, -1, 4096, 16, 1, 16, None) == INV           # negative tile count
+    assert P(16, 1 << 31, 4096, 16, 1, 16, None) == INV      # beyond int32 tile ids
+    assert P(None, 4, 4096, 16, 1, 16, None) == INV
+    assert P(16, 4, 4096, None, 1, 16, None) == INV
+    assert P(16, 4, 4096, 16, 1, None, None) == INV
+    assert P(24, 4, 4096, 16, 1, 16, None) == INV            # misaligned
 
 
 def test_write_and_copy_validation(L):
