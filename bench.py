@@ -35,10 +35,10 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "llama3_8b_gqa_bf16"
-# the decode kernels' code: their source and the headers it includes
+# the decode kernels' code: their source and the library headers with device
+# code or structures they use (the public header only declares the ABI)
 DECODE_SRC = [os.path.join(ROOT, "paged_kv_cache_12_amd", "csrc", f)
-              for f in ("pa_decode.hip", "pa_internal.h", "pa_kv_store.h")] + \
-    [os.path.join(ROOT, "include", "pa.h")]
+              for f in ("pa_decode.hip", "pa_internal.h", "pa_kv_store.h")]
 
 
 def parse():
