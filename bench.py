@@ -257,39 +257,72 @@ def _oracle_rows(rows):
     return len(rows)
 
 
+def replay_sample(sc, samp):
+    """The oracle's pool model and caches for the sequences `samp` of a
+    workload: its op script replayed for them and the sequences they were
+    forked from (creates, forks, frees, appends, copy-on-write copies).
+    Returns (k_cache, v_cache, tables [len(samp)][maxb], lengths)."""
+    from oracle import attention as A
+    from oracle.pool_model import PoolModel
+    wl = sc.wl
+    model = PoolModel(sc.num_blocks, wl.block_size, sc.free_order)
+    st = synth.STORAGE[wl.dtype]
+    kc = np.zeros(A.k_cache_shape(sc.num_blocks, wl.h_kv, wl.block_size, wl.head_dim, wl.dtype), st)
+    vc = np.zeros(A.v_cache_shape(sc.num_blocks, wl.h_kv, wl.block_size, wl.head_dim, wl.dtype), st)
+    keep = set(samp)
+    for op in reversed(sc.ops):
+        if op[0] == "fork" and op[2] in keep:
+            keep.add(op[1])
+
+    def put(seqs, ntok, kv, vv):
+        _, slots, pairs = model.append_batch(seqs, ntok)
+        if pairs:
+            A.copy_blocks(kc, vc, pairs)
+        A.write_kv(kc, vc, kv, vv, slots)
+
+    for op in sc.ops:
+        kind = op[0]
+        if kind == "create" and op[1] in keep:
+            model.create(op[1])
+        elif kind == "fork" and op[2] in keep:
+            model.fork(op[1], op[2])
+        elif kind == "free" and op[1] in keep:
+            model.free_seq(op[1])
+        elif kind == "append" and op[1].seq in keep and op[1].ntok > 0:
+            kv, vv = sc.values(op[1])
+            put([op[1].seq], op[1].ntok, kv, vv)
+        elif kind == "append_rr":
+            runs = [r for r in op[1] if r.seq in keep and r.ntok > 0]
+            vals = {r.seq: sc.values(r) for r in runs}
+            for rr in range(max((r.ntok for r in runs), default=0)):
+                live = [r.seq for r in runs if r.ntok > rr]
+                put(live, 1, np.stack([vals[q][0][rr] for q in live]),
+                    np.stack([vals[q][1][rr] for q in live]))
+    tabs = [model.block_table(s) for s in samp]
+    maxb = max(len(t) for t, _ in tabs)
+    tab = np.full((len(samp), maxb), -1, np.int32)
+    lens = np.array([n for _, n in tabs], np.int32)
+    for i, (t, _) in enumerate(tabs):
+        tab[i, :len(t)] = t
+    return kc, vc, tab, lens
+
+
 def cpu_baseline(sc, budget_s: float, workers: int):
     """Time the oracle (as it stands) on a bounded sample of the same workload.
 
-    Its pool model and cache writes set up the sample; then paged_decode over
-    the sample's sequences is repeated until `budget_s` seconds have passed.
+    Its pool model and cache writes set up the sample (replay_sample); then
+    paged_decode over the sample's sequences is repeated until `budget_s`
+    seconds have passed.
     The sequences are spread over `workers` forked processes (one BLAS thread
     each), which inherit the sample copy-on-write.  Must run before this
     process touches the GPU: the workers are forked, not started afresh."""
     import multiprocessing as mp
     from threadpoolctl import threadpool_limits
-    from oracle import attention as A
-    from oracle.pool_model import PoolModel
     wl = sc.wl
     B = len(sc.decode_seqs)
     nsamp = min(B, max(8, 2 * workers))
     samp = sc.decode_seqs[:nsamp]
-    model = PoolModel(sc.num_blocks, wl.block_size, sc.free_order)
-    st = synth.STORAGE[wl.dtype]
-    kc = np.zeros(A.k_cache_shape(sc.num_blocks, wl.h_kv, wl.block_size, wl.head_dim, wl.dtype), st)
-    vc = np.zeros(A.v_cache_shape(sc.num_blocks, wl.h_kv, wl.block_size, wl.head_dim, wl.dtype), st)
-    for op in sc.ops:
-        if op[0] == "create" and op[1] in samp:
-            model.create(op[1])
-        elif op[0] == "append" and op[1].seq in samp:
-            kv, vv = sc.values(op[1])
-            _, slots, _ = model.append(op[1].seq, op[1].ntok)
-            A.write_kv(kc, vc, kv, vv, slots)
-    tabs = [model.block_table(s) for s in samp]
-    maxb = max(len(t) for t, _ in tabs)
-    tab = np.full((nsamp, maxb), -1, np.int32)
-    lens = np.array([n for _, n in tabs], np.int32)
-    for i, (t, _) in enumerate(tabs):
-        tab[i, :len(t)] = t
+    kc, vc, tab, lens = replay_sample(sc, samp)
     kv_bytes = float(lens.sum()) * 2 * wl.h_kv * wl.head_dim * synth.ELEM_BYTES[wl.dtype]
     _SAMPLE.update(q=sc.q[:nsamp], kc=kc, vc=vc, tab=tab, lens=lens, scale=wl.scale,
                    dtype=wl.dtype)

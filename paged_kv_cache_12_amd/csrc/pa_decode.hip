@@ -107,12 +107,15 @@ struct ChunkSpan {
   int nchunks, t0, t1;
 };
 
-// Chunks covering n tokens (at least one, also for n == 0).
-template <int NW>
-__device__ __forceinline__ int chunks_of(int n, int part) {
+// Chunks of nw partitions covering n tokens (at least one, also for n == 0).
+__device__ __forceinline__ int chunks_n(int n, int part, int nw) {
   if (part <= 0) return 1;
   const int nparts = (n + part - 1) / part;
-  return nparts > NW ? (nparts + NW - 1) / NW : 1;
+  return nparts > nw ? (nparts + nw - 1) / nw : 1;
+}
+template <int NW>
+__device__ __forceinline__ int chunks_of(int n, int part) {
+  return chunks_n(n, part, NW);
 }
 
 // Token range of wave `wave` in chunk `ch` over tokens [lo, hi): partition
@@ -392,22 +395,32 @@ __device__ __forceinline__ void compute_group(GroupTiles<T, D>& G,
 //            32 / G sequences).
 enum { kPlain = 0, kSuffix = 1, kPrefix = 2, kPrefix2 = 3 };
 
-// The prefix pass runs at most kPrefixWaves waves per work-group (its
-// two-tile form's registers allow two waves per SIMD), so its chunks count
-// with that many partitions.
+// The one-tile prefix pass runs at most kPrefixWaves waves per work-group
+// (three work-groups fill a CU's wave slots); the two-tile form, two waves
+// per SIMD, runs twice as many (up to 8: one work-group per CU), so that a
+// 4096-token prefix with 512-token partitions is one chunk and leaves one
+// partial per row, half the partial bytes the suffix pass then reads.  The
+// prefix pass's wave count travels in Cascade::prefix_nw, with which the
+// suffix pass and the reduce count a row's prefix chunks.
 constexpr int kPrefixWaves = 4;
 template <int NW>
 struct PrefixNW {
   static constexpr int value = NW > kPrefixWaves ? kPrefixWaves : NW;
 };
+template <int NW>
+struct Prefix2NW {
+  static constexpr int value = 2 * PrefixNW<NW>::value > 8 ? 8 : 2 * PrefixNW<NW>::value;
+};
 
 // Cascade description on the device: prefix_len[B]; groups[ng][3] =
-// {first member, member count, L}; members[] = sequence indices.
+// {first member, member count, L}; members[] = sequence indices; prefix_nw:
+// waves per work-group of the prefix pass that ran.
 struct Cascade {
   const int32_t* prefix_len;
   const int32_t* groups;
   const int32_t* members;
   int ngroups;
+  int prefix_nw;
 };
 
 template <typename T, int D, int BS, int NW, bool NT, int MODE>
@@ -468,7 +481,7 @@ void decode_part_mfma(
     if constexpr (MODE == kSuffix) {
       lo = cas.prefix_len[s];
       lo = lo < 0 ? 0 : (lo > hi ? hi : lo);
-      if (lo > 0) slot0 = chunks_of<PrefixNW<NW>::value>(lo, part);
+      if (lo > 0) slot0 = chunks_n(lo, part, cas.prefix_nw);
     }
     hin[0] = hg * 16 + c;  // head within the GQA group
     hvalid[0] = hin[0] < G;
@@ -569,7 +582,49 @@ void decode_part_mfma(
     lt[t] = xor_sum(lt[t], 32);
   }
 
-  if constexpr (NW > 1) {
+  if constexpr (PREFIX && NW > 4) {
+    // Merge the waves' states pairwise (a tree, log2 NW rounds): in each
+    // round the upper half of the active waves hands its (m, l, o) through LDS
+    // to the lower half, which combines them with weights 2^(m - M).  Each
+    // wave reads one other state per round, so the merge needs few registers
+    // and its LDS reads are spread over the waves.
+    constexpr int SLOTS = NW / 2;
+    __shared__ float tr_m[SLOTS][TT][16];
+    __shared__ float tr_l[SLOTS][TT][16];
+    __shared__ f32x4 tr_o[SLOTS][TT][NJ][64];
+    for (int active = NW; active > 1;) {  // uniform over the work-group
+      const int half = (active + 1) >> 1;
+      if (wave >= half && wave < active) {
+        const int sl = wave - half;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          if (g == 0) {
+            tr_m[sl][t][c] = m[t];
+            tr_l[sl][t][c] = lt[t];
+          }
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) tr_o[sl][t][j][lane] = o[t][j];
+        }
+      }
+      __syncthreads();
+      if (wave < active - half) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          const float mp = tr_m[wave][t][c], lp = tr_l[wave][t][c];
+          const float mm = fmaxf(m[t], mp);
+          const float f0 = m[t] == -INFINITY ? 0.f : fast_exp2(m[t] - mm);
+          const float f1 = mp == -INFINITY ? 0.f : fast_exp2(mp - mm);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) o[t][j] = f0 * o[t][j] + f1 * tr_o[wave][t][j][lane];
+          lt[t] = f0 * lt[t] + f1 * lp;
+          m[t] = mm;
+        }
+      }
+      __syncthreads();  // the slots are free for the next round
+      active = half;
+    }
+    if (wave > 0) return;
+  } else if constexpr (NW > 1) {
     // Merge the waves' states: M = max m_w, weights 2^(m_w - M).
     __shared__ float sh_m[NW][TT][16];
     __shared__ float sh_l[NW][TT][16];
@@ -804,7 +859,7 @@ template <typename T, int D, int NW>
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce(
     T* __restrict__ out, const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
     const int32_t* __restrict__ ctx_lens, int max_tokens, int H_q, int part, int maxP,
-    const int32_t* __restrict__ prefix_len) {
+    const int32_t* __restrict__ prefix_len, int prefix_nw) {
   constexpr int TPR = D / 4;                  // threads per partition row
   constexpr int PL = kReduceThreads / TPR;    // partition lanes
   __shared__ float sh_w[kReduceChunk];
@@ -822,7 +877,7 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce(
     const int L = prefix_len[s] < ctx ? prefix_len[s] : ctx;
     const int nsuf = chunks_of<NW>(ctx - L, part);
     if (nsuf == 1) return;  // merged by the suffix pass
-    nchunks = chunks_of<PrefixNW<NW>::value>(L, part) + nsuf;
+    nchunks = chunks_n(L, part, prefix_nw) + nsuf;
   } else {
     nchunks = chunks_of<NW>(ctx, part);
     if (nchunks <= 1) return;
@@ -939,36 +994,42 @@ void launch_mfma_nw(const DecodeArgs& a) {
     if (maxC > 1)
       hipLaunchKernelGGL((decode_reduce<T, D, NW>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0,
                          a.st, static_cast<T*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens,
-                         a.H_q, a.part, maxC, nullptr);
+                         a.H_q, a.part, maxC, nullptr, 0);
     return;
   }
   // prefix pass (groups re-read the same blocks: cached loads), then the rest
   // of every sequence, then the merge; row stride maxC + 1 slots
   // (the suffixes are mostly private blocks: streaming loads)
-  constexpr int NWP = PrefixNW<NW>::value;
+  // (the slot stride counts prefix chunks of NWP waves: with more waves per
+  // chunk a row has no more chunks, so the stride, and the workspace size
+  // that assumes it, stay bounds)
+  constexpr int NWP = PrefixNW<NW>::value, NWP2 = Prefix2NW<NW>::value;
+  const bool two = a.max_members * a.G > 16;
+  DecodeArgs b = a;
+  b.cas.prefix_nw = two ? NWP2 : NWP;
   const int stride = host_chunks(a.max_tokens, a.part, NWP) + 1;
-  const int cp = host_chunks(a.max_prefix, a.part, NWP);
+  const int cp = host_chunks(a.max_prefix, a.part, b.cas.prefix_nw);
   // A family wider than one column group (32 / G members) spans several
   // groups that re-read its blocks: cached loads, XCD-aware order.  When the
   // largest group is smaller than that, every group is a whole family and
   // each prefix block is read once: streaming loads, as in the plain pass.
   const bool reread = a.max_members >= 32 / a.G;
-  if (a.max_members * a.G > 16) {
+  if (two) {
     if (reread)
-      launch_part<T, D, BS, NWP, false, kPrefix2>(a, cp, stride, a.cas.ngroups);
+      launch_part<T, D, BS, NWP2, false, kPrefix2>(b, cp, stride, a.cas.ngroups);
     else
-      launch_part<T, D, BS, NWP, true, kPrefix2>(a, cp, stride, a.cas.ngroups);
+      launch_part<T, D, BS, NWP2, true, kPrefix2>(b, cp, stride, a.cas.ngroups);
   } else {
     if (reread)
-      launch_part<T, D, BS, NWP, false, kPrefix>(a, cp, stride, a.cas.ngroups);
+      launch_part<T, D, BS, NWP, false, kPrefix>(b, cp, stride, a.cas.ngroups);
     else
-      launch_part<T, D, BS, NWP, true, kPrefix>(a, cp, stride, a.cas.ngroups);
+      launch_part<T, D, BS, NWP, true, kPrefix>(b, cp, stride, a.cas.ngroups);
   }
-  launch_part<T, D, BS, NW, true, kSuffix>(a, maxC, stride, a.B);
+  launch_part<T, D, BS, NW, true, kSuffix>(b, maxC, stride, a.B);
   if (host_chunks(a.max_rest, a.part, NW) > 1)  // some rest takes several chunks
     hipLaunchKernelGGL((decode_reduce<T, D, NW>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0,
                        a.st, static_cast<T*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens,
-                       a.H_q, a.part, stride, a.cas.prefix_len);
+                       a.H_q, a.part, stride, a.cas.prefix_len, b.cas.prefix_nw);
 }
 
 // Waves per work-group for a partition size (see kChunkTokens).
@@ -1001,7 +1062,7 @@ void launch_f32(const DecodeArgs& a) {
   if (a.maxP > 1)
     hipLaunchKernelGGL((decode_reduce<float, D, 1>), dim3(a.H_q, a.B), dim3(kReduceThreads), 0,
                        a.st, static_cast<float*>(a.out), a.ws_o, a.ws_ml, a.lens, a.max_tokens,
-                       a.H_q, a.part, a.maxP, nullptr);
+                       a.H_q, a.part, a.maxP, nullptr, 0);
 }
 
 template <typename T>
@@ -1107,7 +1168,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   a.maxP = num_partitions(max_context_len, partition_size);
   a.part = a.maxP > 1 ? partition_size : 0;
-  a.cas = Cascade{nullptr, nullptr, nullptr, 0};
+  a.cas = Cascade{nullptr, nullptr, nullptr, 0, 0};
   a.max_prefix = 0;
   a.max_members = 0;
   a.max_rest = 0;
@@ -1118,7 +1179,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   }
   size_t slots = a.maxP;
   if (cascade) {
-    a.cas = Cascade{plan->prefix_len, plan->groups, plan->members, plan->ngroups};
+    a.cas = Cascade{plan->prefix_len, plan->groups, plan->members, plan->ngroups, 0};
     a.max_prefix = plan->max_prefix;
     a.max_members = plan->max_members;
     a.max_rest = plan->max_rest;
