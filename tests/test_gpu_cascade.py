@@ -32,6 +32,8 @@ def _gpu():
 def _workload(name):
     if name == "prefix_g4":
         return synth.WORKLOADS["shared_prefix_bf16"], dict(batch=18, ctx_hi=300)
+    if name == "prefix_g4_long":    # suffixes up to 2500 tokens: several suffix chunks
+        return synth.WORKLOADS["shared_prefix_bf16"], dict(batch=18, ctx_hi=2500)
     if name == "prefix_g4_wide":    # 40 sharers: column groups of 32 and 8 members
         return synth.WORKLOADS["shared_prefix_bf16"], dict(batch=40, ctx_hi=120)
     if name == "cow_g1":
@@ -51,7 +53,11 @@ def _workload(name):
 @pytest.mark.parametrize("name,part", [("prefix_g4", 512), ("prefix_g4", 0), ("prefix_g4", 64),
                                        ("prefix_g4_wide", 512), ("prefix_g4_wide", 32),
                                        ("cow_g1", 512), ("cow_g1", 0), ("prefix_g8_bs32", 96),
-                                       ("prefix_g4_f16_d64", 256), ("prefix_g4_f16_d64", 0)])
+                                       ("prefix_g4_f16_d64", 256), ("prefix_g4_f16_d64", 0),
+                                       # two-tile prefix passes of 4 and 2 waves; rows whose
+                                       # rest spans several chunks go through the reduce
+                                       ("prefix_g4", 2048), ("prefix_g4_long", 1024),
+                                       ("prefix_g4_long", 512)])
 def test_cascade_decode_matches_oracle(name, part):
     import torch
     import paged_kv_cache_12_amd as pa
