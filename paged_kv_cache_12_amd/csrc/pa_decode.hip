@@ -30,12 +30,6 @@
 
 #include "pa_kv_store.h"
 
-#ifndef PA_LAZY
-#define PA_LAZY 1
-#endif
-#ifndef PA_WAVES
-#define PA_WAVES 3
-#endif
 
 namespace pa {
 
@@ -50,6 +44,10 @@ constexpr int kChunkTokens = 2048;
 // 512-token partitions: 477 -> 457 us; shorter ranges lose more to idle waves
 // in a sequence's last chunk than they gain.
 constexpr int kLongParts = 64;
+
+// Waves per SIMD the one-tile kernels are compiled for (at most 168 VGPRs);
+// the two-tile prefix pass needs more registers and runs two.
+constexpr int kWavesPerSimd = 3;
 
 // Scores more than this many log2 units above the running reference trigger a
 // rescale; weights fed to the PV product are at most 2^kRescaleLog2.
@@ -264,7 +262,6 @@ __device__ __forceinline__ typename Mfma<T>::v8 qk_softmax(const GroupTiles<T, D
   float mraw = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                      fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
   const float mloc = mraw * scale_log2;
-#if PA_LAZY
   // Lazy rescale: the reference m only moves when a score exceeds it by more
   // than kRescaleLog2, so weights stay <= 2^kRescaleLog2 and the accumulators
   // are rescaled only on this wave-uniform, rarely taken path.
@@ -288,24 +285,6 @@ __device__ __forceinline__ typename Mfma<T>::v8 qk_softmax(const GroupTiles<T, D
     pop[i] = static_cast<T>(e);
   }
   l += psum;
-#else
-  float mw = xor_max(mloc, 16);
-  mw = xor_max(mw, 32);
-  const float mnew = fmaxf(m, mw);
-  const float alpha = fast_exp2(m - mnew);
-  float psum = 0.f;
-  v8 pop;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float e = fast_exp2(fmaf(x[i], scale_log2, -mnew));
-    psum += e;
-    pop[i] = static_cast<T>(e);
-  }
-  l = l * alpha + psum;
-  m = mnew;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) o[j] *= alpha;
-#endif
   return pop;
 }
 
@@ -425,7 +404,7 @@ struct Cascade {
 
 template <typename T, int D, int BS, int NW, bool NT, int MODE>
 __global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(MODE == kPrefix2 ? 2 : PA_WAVES)))
+__attribute__((amdgpu_waves_per_eu(MODE == kPrefix2 ? 2 : kWavesPerSimd)))
 void decode_part_mfma(
     T* __restrict__ out, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
     const T* __restrict__ q, const T* kc, const T* vc,
