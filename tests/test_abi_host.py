@@ -381,6 +381,34 @@ def _plan_by_definition(tab, lens, bs, G, min_prefix):
     return pre, groups, members, mp, mm, rest()
 
 
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16, 32])
+def test_cascade_plan_cuts_wide_families(L, G):
+    """A family wider than one column group is cut into column groups of
+    32 / G members in table order (none for G > 16); a second family and a
+    loner stay apart."""
+    bs, maxb = 16, 8
+    B = 40 + 5 + 1
+    tab = np.zeros((B, maxb), np.int32)
+    tab[:40] = np.arange(maxb)                 # family A: 40 members, 8 shared blocks
+    tab[40:45] = np.arange(100, 100 + maxb)    # family B: 5 members
+    tab[45] = np.arange(200, 200 + maxb)       # a loner
+    lens = np.full(B, maxb * bs, np.int32)
+    lens[3] = 100                              # caps family A's prefix at 96 tokens
+    got = pa.pa_cascade_plan(tab, lens, bs, 8 * G, 8, 64)
+    pre, groups, members, mp, mm, mr = _plan_by_definition(tab, lens, bs, G, 64)
+    assert got[1].tolist() == groups and got[2].tolist() == members
+    assert got[0].tolist() == pre and (got[3], got[4], got[5]) == (mp, mm, mr)
+    if G <= 16:
+        cap = 32 // G
+
+        def cut(n):
+            return [cap] * (n // cap) + ([n % cap] if n % cap else [])
+        assert [cnt for _, cnt, _ in groups] == cut(40) + cut(5)
+        assert groups[0][2] == 96 and pre[45] == 0
+    else:
+        assert groups == [] and mp == 0
+
+
 @pytest.mark.parametrize("seed,G", [(0, 4), (1, 1), (2, 8), (3, 16), (4, 2)])
 def test_cascade_plan_matches_its_definition(L, seed, G):
     rng = np.random.default_rng(seed)
