@@ -343,8 +343,15 @@ def cpu_baseline(sc, budget_s: float, workers: int):
                     break
     _SAMPLE.clear()
     per_step = el / reps
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                       cpu)
+    except OSError:
+        pass
     return {"value": kv_bytes / per_step / 1e9, "unit": "GB/s", "cores": len(chunks),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu,
             "seq_steps_per_s": nsamp / per_step,
             "sample": f"{nsamp} of {B} sequences of {wl.name} (ctx {int(lens.min())}-"
                       f"{int(lens.max())}), fp64 NumPy paged_decode in {len(chunks)} "
