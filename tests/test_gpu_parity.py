@@ -229,6 +229,26 @@ def test_decode_many_short_sequences(dtype, part):
     say("  max abs", ea, "max rel", er)
 
 
+@pytest.mark.parametrize("dtype,part", [("bf16", 0), ("f32", 32)])
+def test_decode_max_batch(dtype, part):
+    """The largest batch the ABI accepts: 65535 sequences (the launch grid's
+    y / z extent carries the sequence in the fp32 kernel and the reduce),
+    contexts of 0 .. 40 tokens (fp32 with 32-token partitions: the reduce
+    runs over the whole grid).  Sampled rows, the first and the last, against
+    the oracle; every empty context gives a zero row."""
+    B = 65535
+    lens = np.random.default_rng(65535).integers(0, 41, B).tolist()
+    sc = small_scenario(dtype, 2, 1, 64, 16, seed=6553, lens=lens)
+    rows = sorted(set(np.random.default_rng(1).choice(B, 256, replace=False).tolist()) |
+                  {0, B - 1})
+    say("max batch", dtype, part, B)
+    gs, os_, got, ref, rows = run_both(sc, part, rows=rows)
+    ea, er = H.check_attention(got, ref, dtype, rows)
+    zero = [s for s, n in enumerate(lens) if n == 0]
+    assert zero and all(np.all(got[s] == 0) for s in zero)
+    say("  max abs", ea, "max rel", er)
+
+
 def test_decode_is_deterministic_and_placement_invariant():
     import torch
     say("determinism / placement")
