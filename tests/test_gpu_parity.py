@@ -249,6 +249,63 @@ def test_decode_max_batch(dtype, part):
     say("  max abs", ea, "max rel", er)
 
 
+@pytest.mark.parametrize("dtype,part", [("bf16", 0), ("bf16", 512), ("f32", 32)])
+def test_cache_beyond_4gib(dtype, part):
+    """Caches of more than 5 GiB whose pool hands out the highest block ids
+    first, so that every block in use (the block writes, a copy-on-write copy
+    after a fork, the decode's reads) lies more than 4 GiB (and for 16-bit
+    data more than 2^31 elements) past the cache base.  Attention against the
+    oracle on each sequence's tokens in logical order (no host copy of the
+    cache is needed)."""
+    from oracle import attention as A
+    H_q, H_kv, d, bs = 8, 2, 128, 16
+    e = 2 if dtype == "bf16" else 4
+    block_bytes = H_kv * bs * d * e
+    nblocks = (5 << 30) // block_bytes + 64
+    free_order = np.arange(nblocks - 1, -1, -1, dtype=np.int32)   # highest ids first
+    lens = [700, 33, 1500]
+    wl = synth.Workload(name="beyond_4gib", dtype=dtype, batch=4, h_q=H_q, h_kv=H_kv,
+                        head_dim=d, block_size=bs, seed=4044)
+    ops = []
+    for s, n in enumerate(lens):
+        ops += [("create", s), ("append", synth.Run(s, n, s))]
+    # seq 3 forks seq 0, whose last block is partly filled: its first append
+    # copies that block
+    ops += [("fork", 0, 3), ("append", synth.Run(3, 5, 10))]
+    q = synth.normal_array(4044, (77,), (4, H_q, d), dtype)
+    sc = synth.Scenario(wl=wl, num_blocks=nblocks, free_order=free_order, ops=ops,
+                        decode_seqs=[0, 1, 2, 3], q=q)
+    say("cache beyond 4 GiB", dtype, part, nblocks, "blocks of", block_bytes, "bytes")
+    gs = H.GpuSide(sc)
+    H.execute(sc, gs)
+    # each sequence's tokens in logical order
+    toks = {}
+    for op in ops:
+        if op[0] == "create":
+            toks[op[1]] = []
+        elif op[0] == "fork":
+            toks[op[2]] = list(toks[op[1]])
+        else:
+            toks[op[1].seq].append(sc.values(op[1]))
+    assert gs.pool.stats()["copies"] == 1
+    out, tab, lens_d = gs.decode(sc.q, sc.decode_seqs, part)
+    import torch
+    torch.cuda.synchronize()
+    low = (4 << 30) // block_bytes + 1
+    used = [b for i in range(4) for b in tab[i, :-(-int(lens_d[i]) // bs)].tolist()]
+    assert min(used) >= low, (min(used), low)
+    got = to_f64(out, dtype)
+    qf = A.to_f64(sc.q, dtype)
+    ref = np.zeros_like(got)
+    for s in range(4):
+        K = np.concatenate([A.to_f64(kv, dtype) for kv, _ in toks[s]])
+        V = np.concatenate([A.to_f64(vv, dtype) for _, vv in toks[s]])
+        assert K.shape[0] == lens_d[s]
+        ref[s] = A.attention_contiguous(qf[s], K, V, wl.scale)
+    ea, er = H.check_attention(got, ref, dtype, range(4))
+    say("  lowest block", min(used), "max abs", ea, "max rel", er)
+
+
 def test_decode_is_deterministic_and_placement_invariant():
     import torch
     say("determinism / placement")
