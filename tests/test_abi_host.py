@@ -216,6 +216,61 @@ def test_pool_fuzz_bit_exact_against_model(L, seed, bs):
             assert lens[i] == model.fill[s]
 
 
+@pytest.mark.parametrize("seed,bs", [(0, 16), (1, 4), (2, 32), (3, 16)])
+def test_pool_beam_steps_bit_exact_against_model(L, seed, bs):
+    """pa_seq_beam_step against the pool model step by step: families of
+    beams of several widths and lengths (block-aligned or not), parents with
+    no, one or several children, old ids reused as new ids, a non-beam
+    sequence forked from a beam, families retiring, and a pool so small that
+    appends run out of blocks; statuses, slots, copy pairs, tables,
+    refcounts, free list and stats all equal."""
+    rng = random.Random(seed)
+    N = 160 if seed != 3 else 40
+    order = rng.sample(range(N), N)
+    pool, model = pa.Pool(N, bs, order), PoolModel(N, bs, order)
+    fams, nxt, extra = [], 0, []
+    for f in range(5):
+        assert pool.create(nxt) == model.create(nxt) == 0
+        n = rng.choice([bs, 2 * bs + 3, 1, 5 * bs, 3])
+        s1, sl1, _ = pool.append_batch([nxt], n)
+        s2, sl2, _ = model.append_batch([nxt], n)
+        assert s1 == s2 and sl1.tolist() == sl2[:len(sl1)]
+        fams.append([nxt])
+        nxt += 1
+    compare(pool, model)
+    for it in range(60):
+        fams = [f for f in fams if f]
+        if not fams:
+            break
+        fam = rng.choice(fams)
+        width = rng.randint(0 if rng.random() < 0.05 else 1, 6)
+        parents = [rng.choice(fam) for _ in range(width)]
+        if rng.random() < 0.3:
+            # reuse some old ids for the new beams
+            news = rng.sample(fam, min(len(fam), width)) + list(range(nxt, nxt + width))
+            news = news[:width]
+            nxt += width
+        else:
+            news = list(range(nxt, nxt + width))
+            nxt += width
+        s1, sl1, pr1 = pool.beam_step(fam, parents, news)
+        s2, sl2, pr2 = model.beam_step(fam, parents, news)
+        assert s1 == s2, (it, s1, s2)
+        if s1 == 0:
+            assert sl1.tolist() == sl2
+            assert [tuple(x) for x in pr1.tolist()] == [tuple(x) for x in pr2]
+        fams[fams.index(fam)] = list(news) if s1 in (0, pa.PA_ERR_NO_BLOCKS) else fam
+        if rng.random() < 0.1 and fams[0]:
+            # a sequence outside the beams shares a beam's blocks
+            assert pool.fork(fams[0][0], nxt) == model.fork(fams[0][0], nxt)
+            extra.append(nxt)
+            nxt += 1
+        if extra and rng.random() < 0.1:
+            e = extra.pop(0)
+            assert pool.free(e) == model.free_seq(e)
+        compare(pool, model)
+
+
 def test_pool_create_rejects_bad_free_order(L):
     h = ctypes.c_void_p()
     bad = np.array([0, 0, 1], dtype=np.int32)
