@@ -244,20 +244,77 @@ PA_EXPORT pa_status pa_seq_beam_step(pa_pool* p, const int64_t* old_beams, int n
     if (p->seqs.count(new_beams[j]) && !is_old.count(new_beams[j])) return PA_ERR_INVALID;
   }
   ++p->tick;
-  // 1. the new beams map their parents' blocks (before any old beam goes)
-  std::vector<Seq> kids;
-  kids.reserve(n_new);
-  for (int j = 0; j < n_new; ++j) {
-    kids.push_back(olds[is_old[parents[j]]]->second);
-    for (int32_t b : kids.back().table) p->retain(b);
-    p->tokens += kids.back().fill;
-  }
-  // 2. the old beams retire
-  for (int i = 0; i < n_old; ++i) free_impl(p, p->seqs.find(old_beams[i]));
-  // 3. the new beams take their ids
-  for (int j = 0; j < n_new; ++j) {
-    Seq& cs = p->seqs.emplace(new_beams[j], std::move(kids[j])).first->second;
-    if (cs.tracked && p->index) p->index->on_fork(*p, new_beams[j], cs);
+  if (p->index) {
+    // 1. the new beams map their parents' blocks (before any old beam goes)
+    std::vector<Seq> kids;
+    kids.reserve(n_new);
+    for (int j = 0; j < n_new; ++j) {
+      kids.push_back(olds[is_old[parents[j]]]->second);
+      for (int32_t b : kids.back().table) p->retain(b);
+      p->tokens += kids.back().fill;
+    }
+    // 2. the old beams retire
+    for (int i = 0; i < n_old; ++i) free_impl(p, p->seqs.find(old_beams[i]));
+    // 3. the new beams take their ids
+    for (int j = 0; j < n_new; ++j) {
+      Seq& cs = p->seqs.emplace(new_beams[j], std::move(kids[j])).first->second;
+      if (cs.tracked && p->index) p->index->on_fork(*p, new_beams[j], cs);
+    }
+  } else {
+    // Without a prefix index, the same result with less work: the first
+    // child of an old beam takes over its record and its references (no copy
+    // and no retain / release pair), further children copy it, and records
+    // of childless beams are reused for those copies.
+    std::vector<int> nkids(n_old, 0), first_kid(n_old, -1), par(n_new);
+    for (int j = 0; j < n_new; ++j) {
+      const int i = is_old[parents[j]];
+      par[j] = i;
+      if (nkids[i]++ == 0) first_kid[i] = j;
+    }
+    // 1. the further children's references, all before any release (as when
+    //    every child retains first), so no block shared with a childless
+    //    beam reaches zero early
+    for (int i = 0; i < n_old; ++i) {
+      if (nkids[i] < 2) continue;
+      const Seq& s = olds[i]->second;
+      for (int32_t b : s.table)
+        for (int k = 1; k < nkids[i]; ++k) p->retain(b);
+      p->tokens += static_cast<int64_t>(nkids[i] - 1) * s.fill;
+    }
+    // 2. the old beams leave the map; childless ones release their blocks in
+    //    beam order, then in table order, so blocks reach the free list in
+    //    the same order as when every old beam retires after the retains
+    std::vector<std::unordered_map<int64_t, Seq>::node_type> nodes(n_old);
+    for (int i = 0; i < n_old; ++i) nodes[i] = p->seqs.extract(olds[i]);
+    std::vector<int> spare;
+    for (int i = 0; i < n_old; ++i) {
+      if (nkids[i] > 0) continue;
+      Seq& s = nodes[i].mapped();
+      for (int32_t b : s.table) p->release(b);
+      p->tokens -= s.fill;
+      spare.push_back(i);
+    }
+    // 3. the new beams take their ids: further children first (their
+    //    parents' records are still out of the map), then first children
+    size_t next = 0;
+    for (int j = 0; j < n_new; ++j) {
+      const int i = par[j];
+      if (first_kid[i] == j) continue;
+      const Seq& src = nodes[i].mapped();
+      if (next < spare.size()) {
+        auto& nh = nodes[spare[next++]];
+        nh.mapped() = src;
+        nh.key() = new_beams[j];
+        p->seqs.insert(std::move(nh));
+      } else {
+        p->seqs.emplace(new_beams[j], src);
+      }
+    }
+    for (int i = 0; i < n_old; ++i) {
+      if (first_kid[i] < 0) continue;
+      nodes[i].key() = new_beams[first_kid[i]];
+      p->seqs.insert(std::move(nodes[i]));
+    }
   }
   // 4. one token each, copy-on-write in the order given
   return append_batch_impl(p, new_beams, n_new, n_new > 0 ? 1 : 0, tokens, slots_out, pairs_out,
@@ -555,14 +612,13 @@ PA_EXPORT pa_status pa_cascade_plan(const int32_t* block_tables, int max_blocks_
     int min_len = context_lens[f[0]];
     for (int32_t s : f) min_len = std::min(min_len, context_lens[s]);
     const int nb = std::min((min_len + block_size - 1) / block_size, max_blocks_per_seq);
+    // the run of leading entries every member shares with the first: each
+    // row against the first one, contiguously
     const int32_t* t0 = block_tables + static_cast<size_t>(f[0]) * max_blocks_per_seq;
-    int common = 0;
-    for (; common < nb; ++common) {
-      bool same = true;
-      for (size_t i = 1; i < f.size() && same; ++i)
-        same = block_tables[static_cast<size_t>(f[i]) * max_blocks_per_seq + common] ==
-               t0[common];
-      if (!same) break;
+    int common = nb;
+    for (size_t i = 1; i < f.size() && common > 0; ++i) {
+      const int32_t* ti = block_tables + static_cast<size_t>(f[i]) * max_blocks_per_seq;
+      common = static_cast<int>(std::mismatch(t0, t0 + common, ti).first - t0);
     }
     int L = std::min(common * block_size, min_len) & ~31;
     if (L < std::max(min_prefix, 32)) continue;
