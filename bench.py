@@ -570,22 +570,23 @@ def bench_beam(args, width: int = 4):
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     done = [None, None]
-    beams = {p: [p] for p in range(P)}
+    beams = [np.arange(P, dtype=np.int64).reshape(P, 1)]   # [prompt][beam] ids
     nxt = [P]
     copies = []
     host_s = []
     nsteps = [0]
 
     def step():
-        olds, parents, news = [], [], []
-        for p in range(P):
-            olds += beams[p]
-            par = rng.choice(beams[p], size=width).tolist()
-            new = list(range(nxt[0], nxt[0] + width))
-            nxt[0] += width
-            parents += par
-            news += new
-            beams[p] = new
+        # every new beam's parent drawn uniformly from its prompt's beams
+        # (one draw for the whole batch)
+        cur = beams[0]
+        pick = rng.integers(0, cur.shape[1], size=(P, width))
+        olds = cur.reshape(-1)
+        parents = np.take_along_axis(cur, pick, axis=1).reshape(-1)
+        new = np.arange(nxt[0], nxt[0] + P * width, dtype=np.int64).reshape(P, width)
+        nxt[0] += P * width
+        news = new.reshape(-1)
+        beams[0] = new
         j = nsteps[0] & 1
         nsteps[0] += 1
         if done[j] is not None:
