@@ -690,20 +690,27 @@ def main():
         step_k = storage_to_torch(sc.step_k, wl.dtype).to(dev)
         step_v = storage_to_torch(sc.step_v, wl.dtype).to(dev)
         sbytes = pa.pa_decode_step_staging_size(B, maxb)
-        h_stage = [torch.empty(sbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        # four pinned staging buffers in turn and a fence after every second
+        # step: before step i refills buffer i % 4, the newest fence recorded
+        # after step i - 4 (that of step i - 4 or i - 3) has passed
+        h_stage = [torch.empty(sbytes, dtype=torch.uint8, pin_memory=True) for _ in range(4)]
         d_stage = torch.empty(sbytes, dtype=torch.uint8, device=dev)
-        done = [None, None]
+        fences = {}
         fill = int(lens0.sum())
 
         def step(i):
-            j = i & 1
-            if done[j] is not None:
-                done[j].synchronize()      # staging buffer j is free again
+            j = i & 3
+            if i >= 4:
+                k = (i - 4) | 1            # the first fence recorded after step i - 4
+                fences[k].synchronize()
+                for old in [f for f in fences if f < k]:
+                    del fences[old]
             h0 = time.perf_counter()
             pa.pa_decode_step(cache.pool, seqs, step_k, step_v, cache.k_cache, cache.v_cache,
                               q, out, wl.scale, part, maxb, h_stage[j], d_stage, ws)
             host_s.append(time.perf_counter() - h0)
-            done[j] = StagingFence(stream)
+            if i % 2:
+                fences[i] = StagingFence(stream)
             step_bytes.append(float(fill + B * (i + 1)) * 2 * wl.h_kv * wl.head_dim * e)
     else:
         tab_h, len_h = cache.tables(seqs, maxb)
