@@ -562,47 +562,56 @@ void decode_part_mfma(
   }
 
   if constexpr (PREFIX && NW > 4) {
-    // Merge the waves' states pairwise (a tree, log2 NW rounds): in each
-    // round the upper half of the active waves hands its (m, l, o) through LDS
-    // to the lower half, which combines them with weights 2^(m - M).  Each
-    // wave reads one other state per round, so the merge needs few registers
-    // and its LDS reads are spread over the waves.
-    constexpr int SLOTS = NW / 2;
-    __shared__ float tr_m[SLOTS][TT][16];
-    __shared__ float tr_l[SLOTS][TT][16];
-    __shared__ f32x4 tr_o[SLOTS][TT][NJ][64];
-    for (int active = NW; active > 1;) {  // uniform over the work-group
-      const int half = (active + 1) >> 1;
-      if (wave >= half && wave < active) {
-        const int sl = wave - half;
+    // One merge round: every wave's (m, l, o) goes to LDS; after one barrier
+    // each wave combines the NW states for its share of the (tile, 16-dim
+    // chunk) slices with weights 2^(m_w - M) and writes those slices of the
+    // rows' partials itself (non-temporal: read once by a later launch).
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    __shared__ float all_m[NW][TT][16];
+    __shared__ float all_l[NW][TT][16];
+    __shared__ f32x4 all_o[NW][TT][NJ][64];
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-          if (g == 0) {
-            tr_m[sl][t][c] = m[t];
-            tr_l[sl][t][c] = lt[t];
-          }
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) tr_o[sl][t][j][lane] = o[t][j];
-        }
+    for (int t = 0; t < TT; ++t) {
+      if (g == 0) {
+        all_m[wave][t][c] = m[t];
+        all_l[wave][t][c] = lt[t];
       }
-      __syncthreads();
-      if (wave < active - half) {
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-          const float mp = tr_m[wave][t][c], lp = tr_l[wave][t][c];
-          const float mm = fmaxf(m[t], mp);
-          const float f0 = m[t] == -INFINITY ? 0.f : fast_exp2(m[t] - mm);
-          const float f1 = mp == -INFINITY ? 0.f : fast_exp2(mp - mm);
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) o[t][j] = f0 * o[t][j] + f1 * tr_o[wave][t][j][lane];
-          lt[t] = f0 * lt[t] + f1 * lp;
-          m[t] = mm;
-        }
-      }
-      __syncthreads();  // the slots are free for the next round
-      active = half;
+      for (int j = 0; j < NJ; ++j) all_o[wave][t][j][lane] = o[t][j];
     }
-    if (wave > 0) return;
+    __syncthreads();
+    for (int pi = wave; pi < TT * NJ; pi += NW) {  // uniform over the wave
+      const int t = pi / NJ, j = pi - t * NJ;
+      float mw[NW];
+      float mm = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        mw[w] = all_m[w][t][c];
+        mm = fmaxf(mm, mw[w]);
+      }
+      float ls = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - mm);
+        ls = fmaf(f, all_l[w][t][c], ls);
+        acc += f * all_o[w][t][j][lane];
+      }
+      bool valid = false;
+      int64_t row = 0;
+#pragma unroll
+      for (int u = 0; u < TT; ++u)
+        if (u == t) {
+          valid = hvalid[u];
+          row = static_cast<int64_t>(s_col[u]) * H_q + kvh * G + hin[u];
+        }
+      if (!valid) continue;
+      const int64_t slot = row * ws_stride + slot0 + ch;
+      __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(ws_o + slot * D + 16 * j + 4 * g));
+      if (j == 0 && g == 0)
+        __builtin_nontemporal_store(f32x2{mm, ls}, reinterpret_cast<f32x2*>(ws_ml + slot));
+    }
+    return;
   } else if constexpr (NW > 1) {
     // Merge the waves' states: M = max m_w, weights 2^(m_w - M).
     __shared__ float sh_m[NW][TT][16];
