@@ -47,6 +47,14 @@ def _workload(name):
                                  dtype="f16", head_dim=64, h_q=16, h_kv=4, prefix_len=777,
                                  seed=612)
         return wl, dict(batch=9, ctx_hi=100)
+    if name == "prefix_g16":        # one member per 16-column tile, groups of 2, 2, 1
+        wl = dataclasses.replace(synth.WORKLOADS["shared_prefix_bf16"], name="prefix_g16",
+                                 h_q=64, h_kv=4, prefix_len=600, seed=613)
+        return wl, dict(batch=5, ctx_hi=150)
+    if name == "prefix_g2_f16":     # 16 members per group (two tiles), then 5
+        wl = dataclasses.replace(synth.WORKLOADS["shared_prefix_bf16"], name="prefix_g2",
+                                 dtype="f16", h_q=16, h_kv=8, prefix_len=900, seed=614)
+        return wl, dict(batch=21, ctx_hi=130)
     raise ValueError(name)
 
 
@@ -57,7 +65,10 @@ def _workload(name):
                                        # two-tile prefix passes of 4 and 2 waves; rows whose
                                        # rest spans several chunks go through the reduce
                                        ("prefix_g4", 2048), ("prefix_g4_long", 1024),
-                                       ("prefix_g4_long", 512)])
+                                       ("prefix_g4_long", 512),
+                                       # GQA widths 16 and 2 (member = column / G)
+                                       ("prefix_g16", 256), ("prefix_g16", 0),
+                                       ("prefix_g2_f16", 512), ("prefix_g2_f16", 128)])
 def test_cascade_decode_matches_oracle(name, part):
     import torch
     import paged_kv_cache_12_amd as pa
