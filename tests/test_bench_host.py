@@ -52,3 +52,25 @@ def test_replay_sample_matches_full_replay(name):
         Ks, Vs = A.gather_sequence(kc, vc, tab[i], int(lens[i]), wl.dtype)
         Kf, Vf = A.gather_sequence(full.kc, full.vc, ftab[i], int(flens[i]), wl.dtype)
         assert np.array_equal(Ks, Kf) and np.array_equal(Vs, Vf), (name, samp[i])
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_source_hash_follows_code_not_comments(tmp_path, monkeypatch):
+    bench = _bench()
+    base = "int f(int x) {\n  return x + 1;  // one\n}\n/* block\n comment */\n"
+    p = tmp_path / "k.hip"
+    monkeypatch.setattr(bench, "DECODE_SRC", [str(p)])
+    p.write_text(base)
+    h0 = bench.source_hash()
+    p.write_text(base.replace("// one", "// another comment").replace("  return", "\treturn"))
+    assert bench.source_hash() == h0
+    p.write_text(base.replace("x + 1", "x + 2"))
+    assert bench.source_hash() != h0
