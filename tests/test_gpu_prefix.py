@@ -129,3 +129,100 @@ def test_prefix_stream_matches_oracle(kind, dtype, bs, part):
     rows = list(range(len(live)))
     ea, er = H.check_attention(to_f64(out, dtype), ref, dtype, rows)
     say("  live", len(live), "max abs", ea, "max rel", er)
+
+
+@pytest.mark.parametrize("kind", [1, 2])
+def test_prefix_hits_decode_steps(kind):
+    """Requests that hit a long cached system prompt (two tenants by salt),
+    then one-call decode steps over all of them: plain appends (which end
+    the index's tracking), and the cascade over the hits, whose shared
+    prefixes exceed 512 tokens; against the oracle, caches bit-exact."""
+    import torch
+    import paged_kv_cache_12_amd as pa
+    from oracle import attention as A
+    from oracle.pool_model import PoolModel
+    from paged_kv_cache_12_amd.manager import PagedKVCache, storage_to_torch, torch_to_storage
+    from test_gpu_parity import to_f64
+    dtype, bs, part, Hq, Hkv, d = "bf16", 16, 512, 16, 4, 128
+    say("prefix hits + decode steps", "hash" if kind == 1 else "radix")
+    rng = random.Random(500 + kind)
+    N = 500
+    order = np.random.default_rng(50 + kind).permutation(N).astype(np.int32)
+    gpu = PagedKVCache(N, bs, Hkv, d, dtype, free_order=order, guard_blocks=1,
+                       fill_bits=synth.poison_bits(dtype))
+    gpu.enable_prefix_cache(kind)
+    model = PoolModel(N, bs, order)
+    model.enable_prefix_cache(kind)
+    st = synth.STORAGE[dtype]
+    kc = np.empty(A.k_cache_shape(N, Hkv, bs, d, dtype), st)
+    vc = np.empty(A.v_cache_shape(N, Hkv, bs, d, dtype), st)
+    ib = np.uint16
+    kc.view(ib)[...] = synth.poison_bits(dtype)
+    vc.view(ib)[...] = synth.poison_bits(dtype)
+    dev = lambda a: storage_to_torch(a, dtype).cuda()
+    system = [rng.randrange(30000) for _ in range(1100)]
+    live, cached = [], 0
+    for sid in range(12):
+        t = system[:rng.randint(800, 1100)] + [rng.randrange(30000)
+                                               for _ in range(rng.randint(1, 60))]
+        salt = b"tenant-b" if sid % 4 == 3 else b""
+        kv = {}
+
+        def k_of(a, b, t=t, kv=kv):
+            kv["k"], kv["v"] = synth.prefix_values(t, a, b, Hkv, d, dtype)
+            return dev(kv["k"])
+
+        def v_of(a, b, kv=kv):
+            return dev(kv["v"])
+
+        c = gpu.create_cached(sid, t, k_of, v_of, salt)
+        so, co, slots = model.create_cached(sid, t, salt)
+        assert so == 0 and co == c
+        if len(slots):
+            A.write_kv(kc, vc, kv["k"], kv["v"], np.asarray(slots))
+        cached += c
+        live.append(sid)
+    assert cached > 0
+
+    def tables():
+        ts = [model.block_table(s_) for s_ in live]
+        tab = np.full((len(live), maxb), -1, np.int32)
+        lens = np.zeros(len(live), np.int32)
+        for i, (tb, n) in enumerate(ts):
+            tab[i, :len(tb)] = tb
+            lens[i] = n
+        return tab, lens
+
+    B, maxb = len(live), 80
+    tab, lens = tables()
+    plan = pa.pa_cascade_plan(tab, lens, bs, Hq, Hkv, 512)
+    assert len(plan[1]) > 0 and plan[3] >= 512      # the steps take the cascade
+    sbytes = pa.pa_decode_step_staging_size(B, maxb)
+    hs = [torch.empty(sbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    ds = torch.empty(sbytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(pa.pa_decode_cascade_workspace_size(B, Hq, d, maxb * bs, part),
+                         pa.pa_decode_workspace_size(B, Hq, d, maxb * bs, part), 256),
+                     dtype=torch.uint8, device="cuda")
+    seqs = np.asarray(live, dtype=np.int64)
+    for step in range(3):
+        kn = synth.normal_array(60 + kind, (step, 1), (B, Hkv, d), dtype)
+        vn = synth.normal_array(60 + kind, (step, 2), (B, Hkv, d), dtype)
+        q = synth.normal_array(60 + kind, (step, 3), (B, Hq, d), dtype)
+        qd = dev(q)
+        out = torch.empty_like(qd)
+        pa.pa_decode_step(gpu.pool, seqs, dev(kn), dev(vn), gpu.k_cache, gpu.v_cache, qd, out,
+                          1.0 / np.sqrt(d), part, maxb, hs[step % 2], ds, ws)
+        torch.cuda.synchronize()
+        so, sl_o, pr_o = model.append_batch(live, 1)
+        assert so == 0
+        if pr_o:
+            A.copy_blocks(kc, vc, pr_o)
+        A.write_kv(kc, vc, kn, vn, np.asarray(sl_o))
+        tab, lens = tables()
+        ref = A.paged_decode(q, kc, vc, tab, lens, 1.0 / np.sqrt(d), dtype)
+        ea, er = H.check_attention(to_f64(out, dtype), ref, dtype, range(B))
+        say("  step", step, "max abs", ea, "max rel", er)
+    assert gpu.pool.prefix_stats() == model.prefix_stats()
+    kf, vf = torch_to_storage(gpu.k_full, dtype), torch_to_storage(gpu.v_full, dtype)
+    assert np.array_equal(kf[1:1 + N].view(ib), kc.view(ib))
+    assert np.array_equal(vf[1:1 + N].view(ib), vc.view(ib))
