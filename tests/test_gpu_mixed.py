@@ -34,7 +34,8 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("dtype,part,seed", [("bf16", 0, 1), ("f16", 64, 2), ("bf16", 512, 3)])
+@pytest.mark.parametrize("dtype,part,seed", [("bf16", 0, 1), ("f16", 64, 2), ("bf16", 512, 3),
+                                            ("f32", 32, 4)])
 def test_random_operation_mix(dtype, part, seed):
     import torch
     import paged_kv_cache_12_amd as pa
