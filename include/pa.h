@@ -396,7 +396,7 @@ pa_status pa_seq_append_batch(pa_pool* pool, const int64_t* seqs, int n, int tok
                               int64_t* slots_out, int32_t* pairs_out, int* num_pairs_out);
 
 /* Release every block of seq in logical order (host blocks if it is swapped
- * out) and forget seq. */
+ * out) and forget seq.  PA_ERR_UNKNOWN_SEQ if seq is unknown. */
 pa_status pa_seq_free(pa_pool* pool, int64_t seq);
 
 /*
@@ -540,22 +540,27 @@ pa_status pa_seq_append_tokens(pa_pool* pool, const int64_t* seqs, int n, const 
 pa_status pa_prefix_stats(const pa_pool* pool, int64_t* stats_out);
 
 /* Copy seq's block table into out[0..cap); *num_blocks_out, *num_tokens_out get
- * its length and fill.  PA_ERR_INVALID if cap is too small (nothing copied). */
+ * its length and fill (also when cap is too small).  PA_ERR_UNKNOWN_SEQ for an
+ * unknown seq; PA_ERR_INVALID if cap is too small (nothing copied). */
 pa_status pa_seq_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int cap,
                              int* num_blocks_out, int* num_tokens_out);
 
-/* Dense tables for a batch: out [n][maxb] padded with -1, lens_out [n]. */
+/* Dense tables for a batch: out [n][maxb] padded with -1, lens_out [n].
+ * PA_ERR_UNKNOWN_SEQ for an unknown sequence; PA_ERR_INVALID for a swapped-out
+ * one or a table longer than maxb. */
 pa_status pa_pool_block_tables(const pa_pool* pool, const int64_t* seqs, int n, int32_t* out,
                                int maxb, int32_t* lens_out);
 
 /* Refcount of a physical block, or -1 if out of range. */
 int pa_pool_refcount(const pa_pool* pool, int32_t block);
 
-/* Current free list, front first: out[0..cap), *n_out = its length. */
+/* Current free list, front first: out[0..cap), *n_out = its length (also
+ * when cap is too small, which returns PA_ERR_INVALID and copies nothing). */
 pa_status pa_pool_free_list(const pa_pool* pool, int32_t* out, int cap, int* n_out);
 
 /* stats_out[5] = {free blocks, used blocks, shared blocks (refcount > 1),
- * tokens held by live sequences, copy-on-write pairs issued so far}. */
+ * tokens held by live sequences, copy-on-write pairs issued so far}.
+ * PA_ERR_INVALID for a null pointer. */
 pa_status pa_pool_stats(const pa_pool* pool, int64_t* stats_out);
 
 /*

@@ -489,3 +489,38 @@ def test_cascade_plan_matches_its_definition(L, seed, G):
     for first, cnt, Lp in groups.tolist():
         rows = [tab[m, :-(-Lp // bs)] for m in members[first:first + cnt]]
         assert all((r == rows[0]).all() for r in rows) and all(lens[m] >= Lp for m in members[first:first + cnt])
+
+
+def test_pool_query_statuses(L):
+    """The documented statuses of the pool's read-only queries and free."""
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    OK, INV, UNK = pa.PA_OK, pa.PA_ERR_INVALID, pa.PA_ERR_UNKNOWN_SEQ
+    pool = pa.Pool(8, 16, list(range(8)))
+    pool.create(0)
+    pool.append(0, 40)                                   # 3 blocks
+    h = pool._h
+    out = np.full(16, -7, np.int32)
+    lens = np.zeros(1, np.int32)
+    one = np.array([0], np.int64)
+    assert L.pa_pool_block_tables(h, P(np.array([9], np.int64)), 1, P(out), 4, P(lens)) == UNK
+    assert L.pa_pool_block_tables(h, P(one), 1, P(out), 2, P(lens)) == INV   # row too long
+    assert L.pa_pool_block_tables(h, P(one), 1, P(out), 4, P(lens)) == OK
+    assert out[:4].tolist() == [0, 1, 2, -1] and lens[0] == 40
+    nb, nt = ctypes.c_int(-1), ctypes.c_int(-1)
+    out[:] = -7
+    assert L.pa_seq_block_table(h, 0, P(out), 2, ctypes.byref(nb), ctypes.byref(nt)) == INV
+    assert (nb.value, nt.value) == (3, 40) and (out == -7).all()     # sizes, nothing copied
+    assert L.pa_seq_block_table(h, 9, P(out), 8, ctypes.byref(nb), ctypes.byref(nt)) == UNK
+    n = ctypes.c_int(-1)
+    assert L.pa_pool_free_list(h, P(out), 2, ctypes.byref(n)) == INV and n.value == 5
+    assert (out == -7).all()
+    assert L.pa_pool_free_list(h, P(out), 8, ctypes.byref(n)) == OK
+    assert out[:5].tolist() == [3, 4, 5, 6, 7]
+    assert L.pa_pool_stats(h, None) == INV
+    assert L.pa_seq_free(h, 9) == UNK
+    # a swapped-out sequence has no device table
+    pool.set_host_blocks(4)
+    pool.swap_out([0])
+    assert L.pa_pool_block_tables(h, P(one), 1, P(out), 4, P(lens)) == INV
+    assert L.pa_seq_free(h, 0) == OK
+    assert pool.stats()["free"] == 8
