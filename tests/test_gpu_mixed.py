@@ -1,6 +1,6 @@
 """GPU parity under a seeded random mix of the pool's operations: one-call
 decode steps (pool append, staging copy, copy-on-write, block write, decode;
-the cascade whenever forks share 512 or more tokens), forks, frees, swaps out
+fp16 / bf16 steps take the cascade whenever forks share 512 or more tokens), forks, frees, swaps out
 to pinned host memory and back, and beam steps on a subset of the sequences,
 in random order.  Every decode is compared with the oracle's attention over
 the oracle pool's tables, every swap's block pairs with the pool model's, and
@@ -65,7 +65,7 @@ def test_random_operation_mix(dtype, part, seed):
     live = list(range(len(sc.decode_seqs)))   # on the GPU
     swapped = []                               # in host blocks
     nxt = 100
-    counts = dict(step=0, fork=0, free=0, swap_out=0, swap_in=0, beam=0, pairs=0)
+    counts = dict(step=0, fork=0, free=0, swap_out=0, swap_in=0, beam=0, pairs=0, cascade=0)
     calls = 0
 
     def attend(seqs, q, out):
@@ -94,6 +94,10 @@ def test_random_operation_mix(dtype, part, seed):
             os_.write(slots, kn, vn)
             attend(seqs, q, out)
             counts["step"] += 1
+            # the grouping the step planned on (the tables after its append)
+            tab, lens = os_.tables(seqs)
+            if len(pa.pa_cascade_plan(tab, lens, bs, H_q, H_kv, 512)[1]) > 0:
+                counts["cascade"] += 1
         elif r < 0.55 and live and len(live) + len(swapped) < max_live:
             p = rng.choice(live)
             gs.fork(p, nxt)
@@ -159,3 +163,4 @@ def test_random_operation_mix(dtype, part, seed):
     assert_caches_equal(gs, os_)
     say("  ops", counts)
     assert counts["step"] > 0 and counts["pairs"] > 0
+    assert dtype == "f32" or counts["cascade"] > 0   # fp16 / bf16 steps took the cascade
