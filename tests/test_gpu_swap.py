@@ -87,6 +87,36 @@ def test_swap_blocks_bit_exact(dtype, bs, d, pairs_on_host):
     assert np.array_equal(storage(c.v_full, dtype).view(ibits(dtype)), vd.view(ibits(dtype)))
 
 
+
+@pytest.mark.parametrize("dtype,bs,d", [("bf16", 16, 128), ("f32", 32, 64)])
+def test_swap_blocks_device_to_device(dtype, bs, d):
+    """Both caches in device memory (pools of different sizes, one geometry):
+    the chosen blocks arrive bit-exact, nothing else of the destination, its
+    guard blocks included, changes."""
+    import torch
+    from oracle import attention as A
+    from paged_kv_cache_12_amd import pa_swap_blocks
+    from paged_kv_cache_12_amd.manager import PagedKVCache, storage_to_torch
+    say("swap_blocks device to device", dtype, bs, d)
+    Hkv, na, nb = 4, 30, 18
+    a = PagedKVCache(na, bs, Hkv, d, dtype, guard_blocks=1, fill_bits=synth.poison_bits(dtype))
+    b = PagedKVCache(nb, bs, Hkv, d, dtype, guard_blocks=1, fill_bits=synth.poison_bits(dtype))
+    ka = synth.normal_array(6, (1,), tuple(a.k_full.shape), dtype)
+    va = synth.normal_array(6, (2,), tuple(a.v_full.shape), dtype)
+    a.k_full.copy_(storage_to_torch(ka, dtype).cuda())
+    a.v_full.copy_(storage_to_torch(va, dtype).cuda())
+    kb, vb = storage(b.k_full, dtype), storage(b.v_full, dtype)
+    g = np.random.default_rng(4)
+    pairs = np.stack([g.choice(na, 12, replace=False), g.choice(nb, 12, replace=False)],
+                     1).astype(np.int32)
+    pa_swap_blocks(a.k_cache, a.v_cache, b.k_cache, b.v_cache, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    A.swap_blocks(ka[1:1 + na], va[1:1 + na], kb[1:1 + nb], vb[1:1 + nb], pairs.tolist())
+    assert np.array_equal(storage(b.k_full, dtype).view(ibits(dtype)), kb.view(ibits(dtype)))
+    assert np.array_equal(storage(b.v_full, dtype).view(ibits(dtype)), vb.view(ibits(dtype)))
+    assert np.array_equal(storage(a.k_full, dtype).view(ibits(dtype)), ka.view(ibits(dtype)))
+
+
 def test_swap_blocks_rejects_pageable_memory():
     import torch
     import paged_kv_cache_12_amd as pa
