@@ -123,6 +123,8 @@ def test_copy_blocks_bit_exact(dtype, bs, d, Hkv):
     cache.v_cache.copy_(storage_to_torch(vc, dtype).cuda())
     perm = rng.permutation(N)
     pairs = np.stack([perm[:12], perm[12:24]], axis=1).astype(np.int32)   # disjoint src / dst
+    fan = np.stack([np.full(3, perm[0]), perm[24:27]], axis=1).astype(np.int32)
+    pairs = np.concatenate([pairs, fan])      # one source to several fresh blocks (beam steps)
     bad = np.array([[N, perm[30]], [perm[31], -1]], dtype=np.int32)        # skipped
     allp = np.concatenate([pairs, bad])
     pa_copy_blocks(cache.k_cache, cache.v_cache, torch.from_numpy(allp).cuda())
