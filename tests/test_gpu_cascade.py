@@ -47,6 +47,11 @@ def _workload(name):
                                  dtype="f16", head_dim=64, h_q=16, h_kv=4, prefix_len=777,
                                  seed=612)
         return wl, dict(batch=9, ctx_hi=100)
+    if name == "prefix_g4_f16_d64_bs32":   # head dim 64 with block size 32, two tiles
+        wl = dataclasses.replace(synth.WORKLOADS["shared_prefix_bf16"], name="prefix_d64_bs32",
+                                 dtype="f16", head_dim=64, block_size=32, h_q=16, h_kv=4,
+                                 prefix_len=700, seed=615)
+        return wl, dict(batch=10, ctx_hi=120)
     if name == "prefix_g16":        # one member per 16-column tile, groups of 2, 2, 1
         wl = dataclasses.replace(synth.WORKLOADS["shared_prefix_bf16"], name="prefix_g16",
                                  h_q=64, h_kv=4, prefix_len=600, seed=613)
@@ -68,7 +73,9 @@ def _workload(name):
                                        ("prefix_g4_long", 512),
                                        # GQA widths 16 and 2 (member = column / G)
                                        ("prefix_g16", 256), ("prefix_g16", 0),
-                                       ("prefix_g2_f16", 512), ("prefix_g2_f16", 128)])
+                                       ("prefix_g2_f16", 512), ("prefix_g2_f16", 128),
+                                       ("prefix_g4_f16_d64_bs32", 512),
+                                       ("prefix_g4_f16_d64_bs32", 64)])
 def test_cascade_decode_matches_oracle(name, part):
     import torch
     import paged_kv_cache_12_amd as pa
