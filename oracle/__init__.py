@@ -12,8 +12,13 @@ Modules
   pool_model pure-Python block pool with refcounts, fork / append / free and
              copy-on-write, under one fixed allocation policy.
   kv_size    per-token KV-cache size closed form.
+  prefix_cache  chain-hash and radix-tree prefix indexes over the pool model.
 
 Every function is pinned by `-m "not gpu"` tests against something other than
-itself (brute force, invariants, closed forms, values printed on the pages).
-No function here is "parity unpinned".
+itself (brute force, invariants, closed forms, values printed on the pages,
+element-by-element placement through hand-worked offsets).  Of the block
+copies, `copy_blocks` is pinned by whole-block equality of each listed pair
+and unchanged other blocks, `swap_blocks` element by element through the
+hand-worked offsets: the direction of each pair, both K and V, whole blocks,
+untouched blocks, pairs applied in order.
 """

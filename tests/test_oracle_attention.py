@@ -198,6 +198,81 @@ def test_copy_blocks_copies_whole_blocks_in_order():
         assert np.array_equal(kc[b], k0[b]) and np.array_equal(vc[b], v0[b])
 
 
+def _token_values(N, H, bs, d, tag):
+    """A value for every (block, head, token, dim) that names it: distinct
+    across positions and across K / V (tag), exact in fp32."""
+    b, h, t, i = np.meshgrid(np.arange(N), np.arange(H), np.arange(bs), np.arange(d),
+                             indexing="ij")
+    return (tag * 1e6 + b * 1e4 + h * 1e3 + t * 10 + i * 0.0625).astype(np.float32)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_swap_blocks_moves_whole_k_and_v_blocks_from_source_to_destination(bs):
+    """Swap to host memory and back (tonho.wtf, "a ideia": the cache can be
+    swapped to CPU RAM; "como funciona": a preempted sequence comes back by
+    swapping in, all of its blocks).  Every element is checked through the
+    hand-pinned per-element offsets, not through block slicing: a reversed
+    pair direction, a K-only copy, a partial block or a write outside the
+    listed destinations each fail here."""
+    H, d, Ng, Nh = 2, 8, 7, 5
+    x = A.vec_elems("f32")
+    kval = _token_values(Ng, H, bs, d, 1)
+    vval = _token_values(Ng, H, bs, d, 2)
+    gk = np.zeros(A.k_cache_shape(Ng, H, bs, d, "f32"), np.float32)
+    gv = np.zeros(A.v_cache_shape(Ng, H, bs, d, "f32"), np.float32)
+    # fill the device-side cache element by element at the documented offsets
+    gkf, gvf = gk.reshape(-1), gv.reshape(-1)
+    for b in range(Ng):
+        for h in range(H):
+            for t in range(bs):
+                for i in range(d):
+                    gkf[A.k_offset(b, h, t, i, H, bs, d, x)] = kval[b, h, t, i]
+                    gvf[A.v_offset(b, h, t, i, H, bs, d, x)] = vval[b, h, t, i]
+    poison = np.float32(-7.5)
+    hk = np.full(A.k_cache_shape(Nh, H, bs, d, "f32"), poison, np.float32)
+    hv = np.full(A.v_cache_shape(Nh, H, bs, d, "f32"), poison, np.float32)
+    g0k, g0v = gk.copy(), gv.copy()
+
+    out_pairs = [(6, 0), (2, 3), (4, 1)]          # device block -> host block
+    A.swap_blocks(gk, gv, hk, hv, out_pairs)
+    # the source cache is only read
+    assert np.array_equal(gk, g0k) and np.array_equal(gv, g0v)
+    hkf, hvf = hk.reshape(-1), hv.reshape(-1)
+    for src, dst in out_pairs:
+        for h in range(H):
+            for t in range(bs):
+                for i in range(d):
+                    assert hkf[A.k_offset(dst, h, t, i, H, bs, d, x)] == kval[src, h, t, i]
+                    assert hvf[A.v_offset(dst, h, t, i, H, bs, d, x)] == vval[src, h, t, i]
+    # host blocks not listed as a destination keep their contents
+    for b in (2, 4):
+        assert np.all(hk[b] == poison) and np.all(hv[b] == poison)
+
+    # back in, into other device blocks: the round trip restores each block
+    in_pairs = [(0, 5), (3, 0), (1, 1)]            # host block -> device block
+    A.swap_blocks(hk, hv, gk, gv, in_pairs)
+    for (gsrc, _), (_, gdst) in zip(out_pairs, in_pairs):
+        assert np.array_equal(gk[gdst], g0k[gsrc]) and np.array_equal(gv[gdst], g0v[gsrc])
+    for b in (2, 3, 4, 6):
+        assert np.array_equal(gk[b], g0k[b]) and np.array_equal(gv[b], g0v[b])
+
+
+def test_swap_blocks_applies_pairs_in_order():
+    """Pairs are applied one after the other: a destination named twice ends
+    with the second source; one source may feed several destinations."""
+    H, bs, d = 1, 16, 8
+    src_k = _token_values(3, H, bs, d, 1)
+    src_v = _token_values(3, H, bs, d, 2)
+    sk = np.ascontiguousarray(src_k.reshape(A.k_cache_shape(3, H, bs, d, "f32")))
+    sv = np.ascontiguousarray(src_v.reshape(A.v_cache_shape(3, H, bs, d, "f32")))
+    dk = np.zeros(A.k_cache_shape(4, H, bs, d, "f32"), np.float32)
+    dv = np.zeros(A.v_cache_shape(4, H, bs, d, "f32"), np.float32)
+    A.swap_blocks(sk, sv, dk, dv, [(0, 2), (1, 2), (1, 3)])
+    assert np.array_equal(dk[2], sk[1]) and np.array_equal(dv[2], sv[1])
+    assert np.array_equal(dk[3], sk[1]) and np.array_equal(dv[3], sv[1])
+    assert not np.any(dk[:2]) and not np.any(dv[:2])
+
+
 # ----------------------------------------------------------------------------
 # attention: brute force
 # ----------------------------------------------------------------------------
