@@ -246,6 +246,8 @@ def host_cores() -> int:
 
 
 _SAMPLE = {}
+# exit codes of the last cpu_baseline's worker processes (0: ended normally)
+WORKER_EXIT_CODES: list = []
 
 
 def _oracle_rows(rows):
@@ -341,6 +343,12 @@ def cpu_baseline(sc, budget_s: float, workers: int):
                 el = time.perf_counter() - t0
                 if el >= budget_s:
                     break
+            # let the workers finish on their own: leaving the `with` block
+            # alone would terminate() them (SIGTERM)
+            workers_ = list(pool._pool)
+            pool.close()
+            pool.join()
+    WORKER_EXIT_CODES[:] = [w.exitcode for w in workers_]
     _SAMPLE.clear()
     per_step = el / reps
     cpu = "unknown"

@@ -74,3 +74,13 @@ def test_source_hash_follows_code_not_comments(tmp_path, monkeypatch):
     assert bench.source_hash() == h0
     p.write_text(base.replace("x + 1", "x + 2"))
     assert bench.source_hash() != h0
+
+
+def test_cpu_baseline_workers_end_normally():
+    """The oracle baseline's worker processes exit by themselves (exit code
+    0) instead of being terminated by a signal when the pool closes."""
+    bench = _bench()
+    sc = synth.build_scenario(synth.WORKLOADS["llama3_8b_gqa_bf16"], **SHRINK["llama3_8b_gqa_bf16"])
+    res = bench.cpu_baseline(sc, 0.2, 3)
+    assert res["kind"] == "oracle" and res["cores"] == 3 and res["value"] > 0
+    assert bench.WORKER_EXIT_CODES == [0, 0, 0]
