@@ -194,7 +194,8 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  *        are issued to the GPU (a permutation of 0..num_seqs-1, for example
  *        from pa_decode_order).  A scheduling hint: results do not depend on
  *        it; entries outside [0, num_seqs) are skipped
- *   scale  softmax scale (1/sqrt(head_dim) for standard attention)
+ *   scale  softmax scale (1/sqrt(head_dim) for standard attention); must be
+ *          positive and finite, else PA_ERR_INVALID
  *   partition_size  0: one work unit per (sequence, KV head); otherwise the
  *        context is split into partitions of this many tokens (a multiple of
  *        32) whose partial results (running max, sum, unnormalised output)

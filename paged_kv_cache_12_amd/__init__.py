@@ -169,6 +169,55 @@ def cache_geometry(k_cache, v_cache):
     return nb, H, bs, d
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_same_dtype(ref, **tensors):
+    for name, t in tensors.items():
+        if t.dtype != ref.dtype:
+            raise TypeError(f"{name} is {t.dtype}, the cache is {ref.dtype}")
+
+
+def _check_decode_io(out, q, k_cache, v_cache):
+    """Shapes and dtypes of a decode's q / out against the cache; returns
+    (num_blocks, H_kv, block_size, head_dim, B, H_q).  Every check runs before
+    any pointer is taken, so a mismatch never reaches a kernel."""
+    nb, H_kv, bs, d = cache_geometry(k_cache, v_cache)
+    torch_dtype_code(k_cache)
+    _check_same_dtype(k_cache, q=q, out=out)
+    if q.dim() != 3 or q.shape[2] != d:
+        raise ValueError(f"q must be [num_seqs][num_q_heads][{d}], got {tuple(q.shape)}")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out shape {tuple(out.shape)} != q shape {tuple(q.shape)}")
+    B, H_q, _ = q.shape
+    if H_q % H_kv != 0:
+        raise ValueError(f"num_q_heads {H_q} is not a multiple of num_kv_heads {H_kv}")
+    return nb, H_kv, bs, d, B, H_q
+
+
+def _check_tables(block_tables, context_lens, B):
+    torch = _torch()
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables / context_lens shape mismatch")
+
+
+def _check_new_kv(k_new, v_new, k_cache, n, H_kv, d):
+    _check_same_dtype(k_cache, k_new=k_new, v_new=v_new)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (n, H_kv, d):
+            raise ValueError(f"{name} must be [{n}][{H_kv}][{d}], got {tuple(t.shape)}")
+
+
+def _seq_ids(seqs, name: str = "seqs") -> np.ndarray:
+    a = np.ascontiguousarray(seqs, dtype=np.int64)
+    if a.ndim != 1:
+        raise ValueError(f"{name} must be one-dimensional")
+    return a
+
+
 # ----------------------------------------------------------------------------
 # device operations
 # ----------------------------------------------------------------------------
@@ -197,6 +246,8 @@ def pa_copy_blocks(k_cache, v_cache, pairs, stream=None):
     nb, H, bs, d = cache_geometry(k_cache, v_cache)
     if pairs.dtype != torch.int32:
         raise TypeError("pairs must be int32")
+    if pairs.numel() % 2:
+        raise ValueError("pairs must be [num_pairs][2]")
     P = pairs.numel() // 2
     if P == 0:
         return
@@ -216,6 +267,8 @@ def pa_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None):
         raise ValueError("source and destination caches differ in geometry or dtype")
     if pairs.dtype != torch.int32:
         raise TypeError("pairs must be int32")
+    if pairs.numel() % 2:
+        raise ValueError("pairs must be [num_pairs][2]")
     P = pairs.numel() // 2
     if P == 0:
         return
@@ -259,27 +312,19 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
     """out, q [B][H_q][d]; block_tables int32 [B][maxb]; context_lens int32 [B];
     seq_order: optional int32 GPU tensor [B] (issue order of the sequences)."""
     torch = _torch()
-    nb, H_kv, bs, d = cache_geometry(k_cache, v_cache)
-    B, H_q, dq = q.shape
-    if dq != d or out.shape != q.shape:
-        raise ValueError("q / out shape mismatch")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise TypeError("block_tables and context_lens must be int32")
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
-        raise ValueError("block_tables / context_lens shape mismatch")
+    nb, H_kv, bs, d, B, H_q = _check_decode_io(out, q, k_cache, v_cache)
+    _check_tables(block_tables, context_lens, B)
+    if seq_order is not None and (seq_order.dtype != torch.int32 or seq_order.numel() != B):
+        raise ValueError("seq_order must be int32 [B]")
     need = pa_decode_workspace_size(B, H_q, d, max_context_len, partition_size)
     ws_ptr, ws_bytes = None, 0
     if need:
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        if workspace.numel() * workspace.element_size() < need:
+        if _nbytes(workspace) < need:
             raise ValueError("workspace too small")
-        ws_ptr, ws_bytes = _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
-    order_ptr = None
-    if seq_order is not None:
-        if seq_order.dtype != torch.int32 or seq_order.numel() != B:
-            raise ValueError("seq_order must be int32 [B]")
-        order_ptr = _dev_ptr(seq_order, "seq_order")
+        ws_ptr, ws_bytes = _dev_ptr(workspace, "workspace"), _nbytes(workspace)
+    order_ptr = None if seq_order is None else _dev_ptr(seq_order, "seq_order")
     st = lib().pa_decode(_dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
                          _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables"),
                          block_tables.shape[1], _dev_ptr(context_lens, "context_lens"), order_ptr, B,
@@ -338,12 +383,16 @@ def pa_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens, max_
                       flags: int = 0, seq_order=None):
     """pa_decode with a shared-prefix plan (GPU int32 tensors from pa_cascade_plan)."""
     torch = _torch()
-    nb, H_kv, bs, d = cache_geometry(k_cache, v_cache)
-    B, H_q, _ = q.shape
+    nb, H_kv, bs, d, B, H_q = _check_decode_io(out, q, k_cache, v_cache)
+    _check_tables(block_tables, context_lens, B)
     ng = groups.numel() // 3
     for t, name in ((prefix_len, "prefix_len"), (groups, "groups"), (members, "members")):
         if t.dtype != torch.int32:
             raise TypeError(f"{name} must be int32")
+    if prefix_len.numel() != B:
+        raise ValueError("prefix_len must have one entry per sequence")
+    if seq_order is not None and (seq_order.dtype != torch.int32 or seq_order.numel() != B):
+        raise ValueError("seq_order must be int32 [B]")
     st = lib().pa_decode_cascade(
         _dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
         _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables"),
@@ -351,7 +400,7 @@ def pa_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens, max_
         None if seq_order is None else _dev_ptr(seq_order, "seq_order"), B, max_context_len, H_q,
         H_kv, d, bs, nb, float(scale), partition_size, _dev_ptr(prefix_len, "prefix_len"),
         _dev_ptr(groups, "groups"), _dev_ptr(members, "members"), ng, max_prefix, max_members,
-        max_rest, _dev_ptr(workspace, "workspace"), workspace.numel(), torch_dtype_code(q), flags,
+        max_rest, _dev_ptr(workspace, "workspace"), _nbytes(workspace), torch_dtype_code(q), flags,
         _stream_ptr(stream))
     _check(st, "pa_decode_cascade")
 
@@ -365,18 +414,21 @@ def pa_decode_step(pool: "Pool", seqs: np.ndarray, k_new, v_new, k_cache, v_cach
                    dev_staging, workspace, stream=None):
     """seqs: int64 numpy array; host_staging: pinned uint8 CPU tensor; dev_staging,
     workspace: uint8 GPU tensors; the rest GPU tensors as for pa_write_kv / pa_decode."""
-    nb, H_kv, bs, d = cache_geometry(k_cache, v_cache)
-    B, H_q, _ = q.shape
+    nb, H_kv, bs, d, B, H_q = _check_decode_io(out, q, k_cache, v_cache)
+    seqs = _seq_ids(seqs)
+    if seqs.size != B:
+        raise ValueError(f"{seqs.size} sequence ids for {B} query rows")
+    _check_new_kv(k_new, v_new, k_cache, B, H_kv, d)
     if not host_staging.is_pinned():
         raise ValueError("host_staging must be pinned host memory")
-    sbytes = min(host_staging.numel(), dev_staging.numel())
+    sbytes = min(_nbytes(host_staging), _nbytes(dev_staging))
     st = lib().pa_decode_step(pool._h, _np_ptr(seqs), B, _dev_ptr(k_new, "k_new"),
                               _dev_ptr(v_new, "v_new"), _dev_ptr(k_cache, "k_cache"),
                               _dev_ptr(v_cache, "v_cache"), nb, H_kv, d, bs, _dev_ptr(q, "q"),
                               _dev_ptr(out, "out"), H_q, float(scale), partition_size,
                               max_blocks_per_seq, host_staging.data_ptr(),
                               _dev_ptr(dev_staging, "dev_staging"), sbytes,
-                              _dev_ptr(workspace, "workspace"), workspace.numel(),
+                              _dev_ptr(workspace, "workspace"), _nbytes(workspace),
                               torch_dtype_code(q), _stream_ptr(stream))
     _check(st, "pa_decode_step")
 
@@ -388,21 +440,25 @@ def pa_beam_decode_step(pool: "Pool", old_beams, parents, new_beams, k_new, v_ne
     """One beam-search iteration in one native call (pool beam step, staging copy,
     copy-on-write, block write, decode).  Ids: int64 numpy arrays; k_new, v_new
     [len(new_beams)][H_kv][d], q / out [len(new_beams)][H_q][d] GPU tensors."""
-    nb, H_kv, bs, d = cache_geometry(k_cache, v_cache)
-    old = np.ascontiguousarray(old_beams, dtype=np.int64)
-    par = np.ascontiguousarray(parents, dtype=np.int64)
-    new = np.ascontiguousarray(new_beams, dtype=np.int64)
-    H_q = q.shape[1]
+    nb, H_kv, bs, d, B, H_q = _check_decode_io(out, q, k_cache, v_cache)
+    old = _seq_ids(old_beams, "old_beams")
+    par = _seq_ids(parents, "parents")
+    new = _seq_ids(new_beams, "new_beams")
+    if par.size != new.size:
+        raise ValueError("parents and new_beams differ in length")
+    if new.size != B:
+        raise ValueError(f"{new.size} new beams for {B} query rows")
+    _check_new_kv(k_new, v_new, k_cache, B, H_kv, d)
     if not host_staging.is_pinned():
         raise ValueError("host_staging must be pinned host memory")
-    sbytes = min(host_staging.numel(), dev_staging.numel())
+    sbytes = min(_nbytes(host_staging), _nbytes(dev_staging))
     st = lib().pa_beam_decode_step(pool._h, _np_ptr(old), old.size, _np_ptr(par), _np_ptr(new),
                                    new.size, _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
                                    _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
                                    nb, H_kv, d, bs, _dev_ptr(q, "q"), _dev_ptr(out, "out"), H_q,
                                    float(scale), partition_size, max_blocks_per_seq,
                                    host_staging.data_ptr(), _dev_ptr(dev_staging, "dev_staging"),
-                                   sbytes, _dev_ptr(workspace, "workspace"), workspace.numel(),
+                                   sbytes, _dev_ptr(workspace, "workspace"), _nbytes(workspace),
                                    torch_dtype_code(q), _stream_ptr(stream))
     _check(st, "pa_beam_decode_step")
 

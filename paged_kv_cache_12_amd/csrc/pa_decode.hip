@@ -1117,7 +1117,8 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
     return PA_ERR_UNSUPPORTED;
   if (partition_size % 32 != 0) return PA_ERR_INVALID;
-  if (!std::isfinite(scale)) return PA_ERR_INVALID;
+  // the fp16 / bf16 path takes the running max of unscaled scores
+  if (!(scale > 0.f) || !std::isfinite(scale)) return PA_ERR_INVALID;
   if (static_cast<int64_t>(max_context_len) >
       static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return PA_ERR_INVALID;

@@ -94,7 +94,7 @@ pa_status check_dev(const StepDev& a, int n) {
   if (n > 65535 || a.num_q_heads > 65535) return PA_ERR_INVALID;  // the decode's grid limits
   if (a.num_q_heads <= 0 || a.num_kv_heads <= 0 || a.num_q_heads % a.num_kv_heads != 0 ||
       a.num_blocks <= 0 || a.partition_size < 0 || a.partition_size % 32 != 0 ||
-      !std::isfinite(a.scale))
+      !(a.scale > 0.f) || !std::isfinite(a.scale))
     return PA_ERR_INVALID;
   if (!a.k_new || !a.v_new || !a.k_cache || !a.v_cache || !a.q || !a.out) return PA_ERR_INVALID;
   if (!aligned16(a.k_new) || !aligned16(a.v_new) || !aligned16(a.k_cache) ||

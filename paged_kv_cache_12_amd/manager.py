@@ -4,12 +4,17 @@ The vLLM encyclopedia entry (tonho.wtf), section "como funciona", has a single
 central KV-cache manager that hands the block tables to the workers together
 with each iteration's input.  PagedKVCache is that manager for one GPU: the C++
 pool decides slots and copy-on-write pairs, and the device operations
-(pa_copy_blocks, pa_write_kv, pa_decode) run on the caller's stream.  Metadata
-goes to the device through pinned host buffers with asynchronous copies.
+(pa_copy_blocks, pa_write_kv, pa_decode) run on the caller's stream.  Every
+metadata tensor of an operation (slots, pairs, tables, lengths, issue order)
+is allocated and copied to the device on that same stream, so the kernels
+that read it are ordered after its copy, and the caching allocator does not
+hand its memory to other work before that stream has passed them.
 Whole sequences can be swapped out to pinned host blocks and back (same
 entry, "a ideia" and "como funciona").
 """
 from __future__ import annotations
+
+import contextlib
 
 import numpy as np
 
@@ -69,7 +74,17 @@ class PagedKVCache:
         self.v_cache = self.v_full[guard_blocks:guard_blocks + num_blocks]
         self.pool = Pool(num_blocks, block_size, free_order)
         self.device = device
-        self._ws = None
+        self._ws = {}   # decode workspace per stream
+
+    def _on(self, stream):
+        """Run the enclosed allocations, copies and launches on `stream` (the
+        current stream when None)."""
+        if stream is None:
+            return contextlib.nullcontext()
+        return self.torch.cuda.stream(stream)
+
+    def _to_dev(self, a, dtype):
+        return self.torch.from_numpy(np.ascontiguousarray(a, dtype=dtype)).to(self.device)
 
     # -- pool operations ----------------------------------------------------
     def create(self, seq: int):
@@ -102,7 +117,7 @@ class PagedKVCache:
 
     def _pairs_to_device(self, pairs):
         # through pinned memory, so the host does not wait for earlier work on
-        # the stream
+        # the (current) stream
         t = self.torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).pin_memory()
         return t.to(self.device, non_blocking=True)
 
@@ -113,8 +128,9 @@ class PagedKVCache:
         if st != PA_OK:
             raise PAError(st, "pa_seq_swap_out")
         if len(pairs):
-            pa_swap_blocks(self.k_cache, self.v_cache, self.k_host, self.v_host,
-                           self._pairs_to_device(pairs), stream=stream)
+            with self._on(stream):
+                pa_swap_blocks(self.k_cache, self.v_cache, self.k_host, self.v_host,
+                               self._pairs_to_device(pairs))
         return pairs
 
     def swap_in(self, seqs, stream=None):
@@ -124,8 +140,9 @@ class PagedKVCache:
         if st != PA_OK:
             raise PAError(st, "pa_seq_swap_in")
         if len(pairs):
-            pa_swap_blocks(self.k_host, self.v_host, self.k_cache, self.v_cache,
-                           self._pairs_to_device(pairs), stream=stream)
+            with self._on(stream):
+                pa_swap_blocks(self.k_host, self.v_host, self.k_cache, self.v_cache,
+                               self._pairs_to_device(pairs))
         return pairs
 
     # -- prefix reuse -----------------------------------------------------------------
@@ -145,24 +162,18 @@ class PagedKVCache:
             raise PAError(st, "pa_seq_create_cached")
         n = len(tokens)
         if n > cached:
-            ds = self.torch.from_numpy(np.ascontiguousarray(slots)).to(self.device)
-            pa_write_kv(k_of(cached, n), v_of(cached, n), self.k_cache, self.v_cache, ds,
-                        stream=stream)
+            with self._on(stream):
+                pa_write_kv(k_of(cached, n), v_of(cached, n), self.k_cache, self.v_cache,
+                            self._to_dev(slots, np.int64))
         return cached
 
     def append_tokens(self, seqs, tokens, k_new, v_new, stream=None):
         """append() with token ids [len(seqs)][k], so the prefix index keeps
         indexing the blocks these sequences fill."""
-        torch = self.torch
         st, slots, pairs = self.pool.append_tokens(np.asarray(seqs, dtype=np.int64), tokens)
         if st != PA_OK:
             raise PAError(st, "pa_seq_append_tokens")
-        if len(pairs):
-            dp = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device)
-            pa_copy_blocks(self.k_cache, self.v_cache, dp, stream=stream)
-        if len(slots):
-            ds = torch.from_numpy(np.ascontiguousarray(slots)).to(self.device)
-            pa_write_kv(k_new, v_new, self.k_cache, self.v_cache, ds, stream=stream)
+        self._copy_and_write(pairs, slots, k_new, v_new, stream)
         return slots, pairs
 
     # -- beam search ----------------------------------------------------------------
@@ -170,33 +181,31 @@ class PagedKVCache:
         """One beam-search step: new beams fork their parents, old beams retire,
         each new beam gets one position (k_new / v_new [len(new_beams)][H][d]);
         the copy-on-write copies run before the block write."""
-        torch = self.torch
         st, slots, pairs = self.pool.beam_step(old_beams, parents, new_beams, tokens)
         if st != PA_OK:
             raise PAError(st, "pa_seq_beam_step")
-        if len(pairs):
-            dp = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device)
-            pa_copy_blocks(self.k_cache, self.v_cache, dp, stream=stream)
-        if len(slots):
-            ds = torch.from_numpy(np.ascontiguousarray(slots)).to(self.device)
-            pa_write_kv(k_new, v_new, self.k_cache, self.v_cache, ds, stream=stream)
+        self._copy_and_write(pairs, slots, k_new, v_new, stream)
         return slots, pairs
+
+    def _copy_and_write(self, pairs, slots, k_new, v_new, stream):
+        """Copy-on-write copies, then the block write, with their metadata, on
+        `stream`."""
+        with self._on(stream):
+            if len(pairs):
+                pa_copy_blocks(self.k_cache, self.v_cache, self._to_dev(pairs, np.int32))
+            if len(slots):
+                pa_write_kv(k_new, v_new, self.k_cache, self.v_cache,
+                            self._to_dev(slots, np.int64))
 
     # -- append: pool slots, copy-on-write, block write ----------------------
     def append(self, seqs, k: int, k_new, v_new, stream=None):
         """Append k tokens to each sequence in `seqs` (in order).  k_new, v_new:
         GPU tensors [len(seqs)*k][H][d] in the same order.  Runs pa_copy_blocks
         for any copy-on-write pair before pa_write_kv.  Returns (slots, pairs)."""
-        torch = self.torch
         st, slots, pairs = self.pool.append_batch(seqs, k)
         if st != PA_OK:
             raise PAError(st, "pa_seq_append_batch")
-        if len(pairs):
-            dp = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device)
-            pa_copy_blocks(self.k_cache, self.v_cache, dp, stream=stream)
-        if len(slots):
-            ds = torch.from_numpy(np.ascontiguousarray(slots)).to(self.device)
-            pa_write_kv(k_new, v_new, self.k_cache, self.v_cache, ds, stream=stream)
+        self._copy_and_write(pairs, slots, k_new, v_new, stream)
         return slots, pairs
 
     # -- decode ---------------------------------------------------------------
@@ -211,19 +220,28 @@ class PagedKVCache:
         return self.pool.block_tables(seqs, maxb)
 
     def decode(self, q, seqs, scale: float, partition_size: int = 512, out=None, stream=None):
+        """Decode attention of q [len(seqs)][H_q][d] over the sequences' blocks
+        on `stream`.  The workspace is kept per stream: decodes on one stream
+        reuse it in stream order."""
         torch = self.torch
         tables, lens = self.tables(seqs)
         max_ctx = int(lens.max()) if lens.size else 0
-        bt = torch.from_numpy(tables).to(self.device)
-        ln = torch.from_numpy(lens).to(self.device)
-        if out is None:
-            out = torch.empty_like(q)
-        need = pa_decode_workspace_size(q.shape[0], q.shape[1], self.d, max_ctx, partition_size)
-        if need and (self._ws is None or self._ws.numel() < need):
-            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         flags = PA_DECODE_SHARED_KV if self.pool.stats()["shared"] > 0 else 0
-        order = torch.from_numpy(pa_decode_order(tables, lens)).to(self.device)
-        pa_decode(out, q, self.k_cache, self.v_cache, bt, ln, max_ctx, scale, partition_size,
-                  workspace=self._ws if need else None, stream=stream, flags=flags,
-                  seq_order=order)
+        order = pa_decode_order(tables, lens)
+        with self._on(stream):
+            cur = torch.cuda.current_stream(self.device)
+            bt = self._to_dev(tables, np.int32)
+            ln = self._to_dev(lens, np.int32)
+            d_order = self._to_dev(order, np.int32)
+            if out is None:
+                out = torch.empty_like(q)
+            need = pa_decode_workspace_size(q.shape[0], q.shape[1], self.d, max_ctx,
+                                            partition_size)
+            ws = self._ws.get(cur.cuda_stream)
+            if need and (ws is None or ws.numel() < need):
+                ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+                self._ws[cur.cuda_stream] = ws
+            pa_decode(out, q, self.k_cache, self.v_cache, bt, ln, max_ctx, scale,
+                      partition_size, workspace=ws if need else None, flags=flags,
+                      seq_order=d_order)
         return out, tables, lens

@@ -117,19 +117,25 @@ class GpuSide:
         assert st == 0, st
         return slots.copy(), pairs.copy()
 
+    def _on(self):
+        # the inputs' copies and the kernels on the side's stream, in order
+        return self.cache._on(self.stream)
+
     def copy(self, pairs):
         from paged_kv_cache_12_amd import pa_copy_blocks
-        dp = self.torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).cuda()
-        pa_copy_blocks(self.cache.k_cache, self.cache.v_cache, dp, stream=self.stream)
+        with self._on():
+            dp = self.torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).cuda()
+            pa_copy_blocks(self.cache.k_cache, self.cache.v_cache, dp)
 
     def write(self, slots, kv, vv):
         from paged_kv_cache_12_amd import pa_write_kv
         from paged_kv_cache_12_amd.manager import storage_to_torch
         t = self.torch
-        ds = t.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).cuda()
-        kd = storage_to_torch(kv, self.wl.dtype).cuda()
-        vd = storage_to_torch(vv, self.wl.dtype).cuda()
-        pa_write_kv(kd, vd, self.cache.k_cache, self.cache.v_cache, ds, stream=self.stream)
+        with self._on():
+            ds = t.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).cuda()
+            kd = storage_to_torch(kv, self.wl.dtype).cuda()
+            vd = storage_to_torch(vv, self.wl.dtype).cuda()
+            pa_write_kv(kd, vd, self.cache.k_cache, self.cache.v_cache, ds)
 
     def enable_swap(self, n):
         self.cache.enable_swap(n)
@@ -151,7 +157,8 @@ class GpuSide:
 
     def decode(self, q_storage, seqs, partition_size, out=None):
         from paged_kv_cache_12_amd.manager import storage_to_torch
-        q = storage_to_torch(q_storage, self.wl.dtype).cuda()
+        with self._on():
+            q = storage_to_torch(q_storage, self.wl.dtype).cuda()
         out, tab, lens = self.cache.decode(q, seqs, self.wl.scale, partition_size, out=out,
                                            stream=self.stream)
         return out, tab, lens

@@ -92,6 +92,9 @@ def test_decode_validation(L):
     assert _decode(L, dt=5) == UNS
     assert _decode(L, part=100) == INV                 # not a multiple of 32
     assert _decode(L, scale=float("inf")) == INV
+    assert _decode(L, scale=float("nan")) == INV
+    assert _decode(L, scale=0.0) == INV                # the running max needs scale > 0
+    assert _decode(L, scale=-0.1) == INV
     assert _decode(L, max_ctx=8 * 16 + 1) == INV       # exceeds maxb * bs
     assert _decode(L, q=None) == INV
     assert _decode(L, out=24) == INV                   # misaligned
@@ -333,6 +336,8 @@ def test_decode_step_rejects_before_touching_the_pool(L):
     assert _step(L, pool, [0, 7]) == pa.PA_ERR_UNKNOWN_SEQ
     assert _step(L, pool, [0, 0]) == INV                  # duplicate ids (append rejects)
     assert _step(L, pool, [0, 1], H_q=70000, H_kv=2) == INV   # beyond the decode's grid
+    assert _step(L, pool, [0, 1], scale=0.0) == INV
+    assert _step(L, pool, [0, 1], scale=-1.0) == INV
     full = pa.Pool(2, 16, [0, 1])
     full.create(0)
     full.append(0, 32)
