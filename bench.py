@@ -34,7 +34,16 @@ import numpy as np  # noqa: E402
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = "llama3_8b_gqa_bf16"
+# the headline line: the long-context 70B-class workload (the largest that the
+# 70 %-of-peak target names); the Llama-3-8B-class step is measured in the same
+# run and nested in the line under its own name
+DEFAULT_WORKLOAD = "long_70b_gqa_bf16"
+DEFAULT_ALSO = "llama3_8b_gqa_bf16"
+# keys of a nested workload record
+NESTED_KEYS = ("value", "unit", "ms_per_step", "pct_of_hbm_peak", "seq_steps_per_s", "dtype",
+               "config", "decode_ms_mean", "decode_cold_copies",
+               "decode_ms_per_call_p10_median_p90", "host_us_per_step", "copy_blocks",
+               "roofline", "read_ceiling", "cpu_baseline")
 # the decode kernels' code: their source and the library headers with device
 # code or structures they use (the public header only declares the ABI)
 DECODE_SRC = [os.path.join(ROOT, "paged_kv_cache_12_amd", "csrc", f)
@@ -47,6 +56,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--also", default=None, choices=sorted(synth.WORKLOADS) + ["none"],
+                    help="a second workload measured in the same run and nested in the line "
+                         f"(default: {DEFAULT_ALSO} with the default --workload, else none)")
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -657,12 +669,25 @@ def main():
     if args.beam:
         bench_beam(args)
         return
-    wl = synth.WORKLOADS[args.workload]
-    part = wl.partition if args.partition is None else args.partition
-    sc = synth.build_scenario(wl)
+    also = args.also or (DEFAULT_ALSO if args.workload == DEFAULT_WORKLOAD else "none")
+    names = [args.workload] + ([also] if also not in ("none", args.workload) else [])
+    scs = {n: synth.build_scenario(synth.WORKLOADS[n]) for n in names}
     # the oracle on the host first: its workers are forked before any GPU use
-    cpu = None if args.no_cpu_baseline else cpu_baseline(
-        sc, args.cpu_seconds, args.cpu_workers or host_cores())
+    cpus = {n: None if args.no_cpu_baseline else
+            cpu_baseline(scs[n], args.cpu_seconds, args.cpu_workers or host_cores())
+            for n in names}
+    res = run_workload(args, scs[names[0]], cpus[names[0]], args.partition)
+    for n in names[1:]:
+        sub = run_workload(args, scs[n], cpus[n], None)
+        res[n] = {k: sub[k] for k in NESTED_KEYS if k in sub}
+    print(json.dumps(res), flush=True)
+
+
+def run_workload(args, sc, cpu, partition):
+    """Time `args.steps` steps of one workload (after `args.warmup`), then
+    its decode alone, cache cold; returns the JSON record."""
+    wl = sc.wl
+    part = wl.partition if partition is None else partition
     import torch
     import paged_kv_cache_12_amd as pa
     from paged_kv_cache_12_amd.manager import PagedKVCache, storage_to_torch
@@ -888,7 +913,13 @@ def main():
     }
     if cpu is not None:
         res["cpu_baseline"] = cpu
-    print(json.dumps(res), flush=True)
+    # release this workload's device memory before the next one
+    del cache, q, out, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 
 
 if __name__ == "__main__":

@@ -148,8 +148,10 @@ WORKLOADS = {
     "long_70b_gqa_bf16": Workload(
         name="long_70b_gqa_bf16", dtype="bf16", batch=8, h_q=64, h_kv=8, head_dim=128,
         block_size=32, seed=104, ctx_lo=32768, ctx_hi=131072, partition=512,
+        step_append=True,
         description="70B-class layer: 64 q / 8 kv heads, d 128, bs 32, batch 8, "
-                    "ctx U[32768,131072], 512-token split-K partitions"),
+                    "ctx U[32768,131072] + one appended token per step, 512-token "
+                    "split-K partitions"),
     "shared_prefix_bf16": Workload(
         name="shared_prefix_bf16", dtype="bf16", batch=256, h_q=32, h_kv=8, head_dim=128,
         block_size=16, seed=105, kind="prefix", prefix_len=4096, ctx_lo=64, ctx_hi=1024,

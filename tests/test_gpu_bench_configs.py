@@ -1,9 +1,10 @@
 """GPU parity in the launch configurations bench.py times, at the workloads'
-full sizes: the Llama-3-8B-class decode step (pa_decode_step: pool append,
-one metadata copy, decode with the block write folded in) and the cascade
+full sizes: the Llama-3-8B-class and long-context 70B-class decode steps
+(pa_decode_step: pool append, one metadata copy, decode with the block write
+folded in; split-K partitions and their reduce for the long contexts) and the cascade
 decode (pa_decode_cascade with the planner's groups, shared-block flag and
-issue order) of the two workloads whose sequences share blocks.  Sampled
-rows against the oracle; caches bit-exact."""
+issue order) of the two workloads whose sequences share blocks.  Every row
+against the oracle; caches bit-exact."""
 import sys
 
 import numpy as np
@@ -11,7 +12,7 @@ import pytest
 
 import synth
 import harness as H
-from test_gpu_parity import _rows, assert_caches_equal, to_f64
+from test_gpu_parity import _rows, assert_caches_equal, check_rows_streamed, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -53,12 +54,13 @@ def _filled(name):
     return wl, sc, gs, os_
 
 
-def test_llama_decode_step_full_size():
+@pytest.mark.parametrize("name", ["llama3_8b_gqa_bf16", "long_70b_gqa_bf16"])
+def test_decode_step_full_size(name):
     import torch
     import paged_kv_cache_12_amd as pa
     from paged_kv_cache_12_amd.manager import storage_to_torch
-    say("decode step at full size: llama3_8b_gqa_bf16")
-    wl, sc, gs, os_ = _filled("llama3_8b_gqa_bf16")
+    say("decode step at full size:", name)
+    wl, sc, gs, os_ = _filled(name)
     seqs = np.asarray(sc.decode_seqs, dtype=np.int64)
     B = seqs.size
     _, lens0 = gs.cache.tables(list(seqs))
@@ -81,8 +83,8 @@ def test_llama_decode_step_full_size():
     assert_caches_equal(gs, os_)
     say("  caches bit-exact after the step")
     rows = _rows(wl, sc)
-    ref = os_.decode(sc.q, sc.decode_seqs, rows)
-    ea, er = H.check_attention(to_f64(out, wl.dtype), ref, wl.dtype, rows)
+    ea, er = check_rows_streamed(os_, sc, out, wl.dtype, rows,
+                                 chunk=1 if wl.partition else 64)
     say("  rows", len(rows), "max abs", ea, "max rel", er)
 
 
@@ -111,6 +113,5 @@ def test_cascade_decode_full_size(name):
                          seq_order=dev(pa.pa_decode_order(tab, lens)))
     torch.cuda.synchronize()
     rows = _rows(wl, sc)
-    ref = os_.decode(sc.q, seqs, rows)
-    ea, er = H.check_attention(to_f64(out, wl.dtype), ref, wl.dtype, rows)
+    ea, er = check_rows_streamed(os_, sc, out, wl.dtype, rows, chunk=64)
     say("  groups", len(groups), "prefix", mp, "rows", len(rows), "max abs", ea, "max rel", er)
