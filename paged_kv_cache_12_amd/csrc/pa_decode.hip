@@ -1034,11 +1034,16 @@ inline int waves_per_group(int part) {
   return want >= 8 ? 8 : want >= 4 ? 4 : want >= 2 ? 2 : 1;
 }
 
+// Waves per work-group of the plain or suffix pass: 6 instead of 4 for long
+// contexts without a cascade (see kLongParts).
+inline int pass_waves(int part, int maxP, bool cascade) {
+  const int nw = waves_per_group(part);
+  return nw == 4 && !cascade && maxP >= kLongParts ? 6 : nw;
+}
+
 template <typename T, int D, int BS>
 void launch_mfma(const DecodeArgs& a) {
-  int nw = waves_per_group(a.part);
-  if (nw == 4 && a.cas.ngroups == 0 && a.maxP >= kLongParts) nw = 6;
-  switch (nw) {
+  switch (pass_waves(a.part, a.maxP, a.cas.ngroups > 0)) {
     case 8: launch_mfma_nw<T, D, BS, 8>(a); break;
     case 6: launch_mfma_nw<T, D, BS, 6>(a); break;
     case 4: launch_mfma_nw<T, D, BS, 4>(a); break;
@@ -1066,6 +1071,34 @@ void dispatch_mfma(const DecodeArgs& a, int D, int BS) {
   else if (D == 64 && BS == 32) launch_mfma<T, 64, 32>(a);
   else if (D == 128 && BS == 16) launch_mfma<T, 128, 16>(a);
   else launch_mfma<T, 128, 32>(a);
+}
+
+// Partial slots per (sequence, query head) row that a decode writes: one per
+// partition on the fp32 path, one per chunk of the plain pass, and with a
+// cascade the prefix chunks (counted at the one-tile pass's wave count, an
+// upper bound) plus one for the rest; 0 when no row has more than one.
+inline int workspace_slots(int dtype, int max_context_len, int partition_size, bool cascade) {
+  const int maxP = num_partitions(max_context_len, partition_size);
+  const int part = maxP > 1 ? partition_size : 0;
+  if (cascade)
+    return host_chunks(max_context_len, part, std::min(waves_per_group(part), kPrefixWaves)) + 1;
+  if (dtype == PA_F32) return maxP > 1 ? maxP : 0;
+  const int maxC = num_chunks(maxP, pass_waves(part, maxP, false));
+  return maxC > 1 ? maxC : 0;
+}
+
+// Workspace layout: fp32 o[rows][slots][head_dim] (256-byte aligned size),
+// then float2 (m, l)[rows][slots].
+struct WsLayout {
+  size_t o_bytes, total;
+};
+inline WsLayout workspace_layout(size_t rows, int slots, int head_dim) {
+  WsLayout w{0, 0};
+  if (slots <= 0) return w;
+  const size_t n = rows * static_cast<size_t>(slots);
+  w.o_bytes = (n * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  w.total = w.o_bytes + n * sizeof(float2);
+  return w;
 }
 
 
@@ -1137,12 +1170,13 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
                   plan->max_members * (num_q_heads / num_kv_heads) > 32 ||
                   plan->max_rest < 0 || plan->max_rest > max_context_len))
     return PA_ERR_INVALID;
-  const size_t need =
-      cascade ? pa_decode_cascade_workspace_size(num_seqs, num_q_heads, head_dim,
-                                                 max_context_len, partition_size)
-              : pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
-                                         partition_size);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+  // exactly the partial slots this call writes (pa_decode_workspace_size and
+  // pa_decode_cascade_workspace_size give bounds of it)
+  const WsLayout ws = workspace_layout(static_cast<size_t>(num_seqs) * num_q_heads,
+                                       workspace_slots(dtype, max_context_len, partition_size,
+                                                       cascade),
+                                       head_dim);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned16(workspace)))
     return PA_ERR_INVALID;
 
   DecodeArgs a;
@@ -1173,19 +1207,15 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
     if (!aligned16(nkv->k) || !aligned16(nkv->v)) return PA_ERR_INVALID;
     a.nkv = *nkv;
   }
-  size_t slots = a.maxP;
   if (cascade) {
     a.cas = Cascade{plan->prefix_len, plan->groups, plan->members, plan->ngroups, 0};
     a.max_prefix = plan->max_prefix;
     a.max_members = plan->max_members;
     a.max_rest = plan->max_rest;
-    slots = host_chunks(max_context_len, a.part, std::min(waves_per_group(a.part), kPrefixWaves)) + 1;
   }
-  if (need > 0) {
-    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * slots;
-    const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  if (ws.total > 0) {
     a.ws_o = static_cast<float*>(workspace);
-    a.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + o_bytes);
+    a.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + ws.o_bytes);
   } else {
     a.ws_o = nullptr;
     a.ws_ml = nullptr;
