@@ -67,7 +67,8 @@ typedef enum {
   PA_ERR_UNSUPPORTED = 2,
   PA_ERR_NO_BLOCKS = 3,
   PA_ERR_UNKNOWN_SEQ = 4,
-  PA_ERR_HIP = 5
+  PA_ERR_HIP = 5,
+  PA_ERR_TOO_LARGE = 6 /* beyond pa_decode_noalloc's fixed scratch */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -217,6 +218,38 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                     int num_blocks, float scale, int partition_size, void* workspace,
                     size_t workspace_bytes, int dtype, int flags, void* stream);
+
+/*
+ * pa_decode_noalloc — pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, semantics and results as pa_decode
+ * (bit-identical: the same kernels), without workspace arguments: the
+ * split-K partials go to a device array of PA_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * that the library holds on each GPU it runs on until the process ends.  The
+ * array's address is looked up once per device, on the first call that needs
+ * it with that device current; nothing is allocated or freed, here or later.
+ *
+ * Limit: the call's partials, num_seqs x num_q_heads x slots x
+ * (4 x head_dim + 8) bytes with one slot per chunk of partitions that a row
+ * spans (at most one per partition), must fit PA_NOALLOC_SCRATCH_BYTES;
+ * otherwise PA_ERR_TOO_LARGE and nothing runs.  Any call for which
+ * pa_decode_workspace_size() is at most PA_NOALLOC_SCRATCH_BYTES fits (the
+ * long-context 70B-class batch of 8 x 64 heads x 131072 tokens in 512-token
+ * partitions needs about 11 MB).
+ *
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (several streams, several host threads without ordering) race on it
+ * and must be serialised by the caller.  Its contents on entry are never
+ * read before being written.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* context_lens, const int32_t* seq_order,
+                            int num_seqs, int max_context_len, int num_q_heads,
+                            int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                            float scale, int partition_size, int dtype, int flags,
+                            void* stream);
 
 /*
  * pa_decode_order — the issue order pa_decode_step gives pa_decode (host

@@ -21,7 +21,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libpa.so")
 
-PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_UNKNOWN_SEQ, PA_ERR_HIP = range(6)
+(PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_UNKNOWN_SEQ, PA_ERR_HIP,
+ PA_ERR_TOO_LARGE) = range(7)
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_DECODE_SHARED_KV = 1
 PA_PREFIX_HASH, PA_PREFIX_RADIX = 1, 2
@@ -38,6 +40,8 @@ SIGNATURES = {
     "pa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "pa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                        _i, _vp, _sz, _i, _i, _vp]),
+    "pa_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                               _i, _f, _i, _i, _i, _vp]),
     "pa_decode_order": (_i, [_vp, _i, _vp, _i, _vp]),
     "pa_cascade_plan": (_i, [_vp, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp]),
@@ -332,6 +336,28 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
                          ws_ptr, ws_bytes, torch_dtype_code(q), flags, _stream_ptr(stream))
     _check(st, "pa_decode")
     return workspace
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens,
+                      max_context_len: int, scale: float, partition_size: int = 512,
+                      stream=None, flags: int = 0, seq_order=None):
+    """pa_decode without a workspace argument: the partials go to the
+    library's fixed per-GPU scratch (PA_NOALLOC_SCRATCH_BYTES); nothing is
+    allocated.  Calls that overlap on one GPU race on that scratch."""
+    torch = _torch()
+    nb, H_kv, bs, d, B, H_q = _check_decode_io(out, q, k_cache, v_cache)
+    _check_tables(block_tables, context_lens, B)
+    if seq_order is not None and (seq_order.dtype != torch.int32 or seq_order.numel() != B):
+        raise ValueError("seq_order must be int32 [B]")
+    order_ptr = None if seq_order is None else _dev_ptr(seq_order, "seq_order")
+    st = lib().pa_decode_noalloc(_dev_ptr(out, "out"), _dev_ptr(q, "q"),
+                                 _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                 _dev_ptr(block_tables, "block_tables"), block_tables.shape[1],
+                                 _dev_ptr(context_lens, "context_lens"), order_ptr, B,
+                                 max_context_len, H_q, H_kv, d, bs, nb, float(scale),
+                                 partition_size, torch_dtype_code(q), flags,
+                                 _stream_ptr(stream))
+    _check(st, "pa_decode_noalloc")
 
 
 def pa_decode_order(block_tables: np.ndarray, context_lens: np.ndarray) -> np.ndarray:

@@ -27,6 +27,7 @@
 // MFMA 16x16x32 operand layout (lane l, g = l / 16, c = l % 16):
 //   A[row c][k 8g..8g+7], B[k 8g..8g+7][col c], D[row 4g+r][col c], r = 0..3.
 #include <algorithm>
+#include <mutex>
 
 #include "pa_kv_store.h"
 
@@ -1268,4 +1269,78 @@ PA_EXPORT pa_status pa_decode_cascade(void* out, const void* q, const void* k_ca
                      num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, flags,
                      seq_order, stream, &plan, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// pa_decode_noalloc: pa_decode with its split-K partials in a fixed device
+// array owned by the library, for callers that cannot allocate.
+// ---------------------------------------------------------------------------
+
+namespace pa {
+
+constexpr size_t kScratchBytes = static_cast<size_t>(PA_NOALLOC_SCRATCH_BYTES);
+constexpr int kMaxDevices = 64;
+
+}  // namespace pa
+
+// One copy per GPU the library runs on, held until the process ends.  Host
+// code never passes this name to a kernel: it stands for the host-side
+// shadow, not the device address, which scratch_address() looks up.
+static __device__ __align__(256) unsigned char scratch[pa::kScratchBytes];
+
+namespace pa {
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+pa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return PA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return PA_ERR_HIP;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+PA_EXPORT pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      int max_blocks_per_seq, const int32_t* context_lens,
+                                      const int32_t* seq_order, int num_seqs,
+                                      int max_context_len, int num_q_heads, int num_kv_heads,
+                                      int head_dim, int block_size, int num_blocks, float scale,
+                                      int partition_size, int dtype, int flags, void* stream) {
+  // the partials this call writes, before anything touches the device
+  size_t need = 0;
+  if (num_seqs > 0 && num_q_heads > 0 && head_dim > 0 && max_context_len >= 0 &&
+      partition_size >= 0)
+    need = workspace_layout(static_cast<size_t>(num_seqs) * num_q_heads,
+                            workspace_slots(dtype, max_context_len, partition_size, false),
+                            head_dim)
+               .total;
+  if (need > kScratchBytes) return PA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const pa_status st = scratch_address(&ws);
+    if (st != PA_OK) return st;
+  }
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, scale, partition_size, ws, ws ? kScratchBytes : 0, dtype, flags,
+                     seq_order, stream, nullptr, nullptr);
 }

@@ -662,6 +662,7 @@ PA_EXPORT const char* pa_status_str(int status) {
     case PA_ERR_NO_BLOCKS: return "not enough free blocks";
     case PA_ERR_UNKNOWN_SEQ: return "unknown sequence id";
     case PA_ERR_HIP: return "HIP launch or runtime error";
+    case PA_ERR_TOO_LARGE: return "request exceeds the fixed no-allocation scratch";
     default: return "unknown status";
   }
 }

@@ -33,7 +33,7 @@ def L():
 
 def test_library_exports_exactly_the_header_functions(L):
     declared = header_functions()
-    assert len(declared) == 41
+    assert len(declared) == 42
     for name in declared:
         assert hasattr(L, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
@@ -48,6 +48,7 @@ def test_library_exports_exactly_the_header_functions(L):
 def test_status_strings(L):
     assert pa.status_str(0) == "ok"
     assert pa.status_str(3) == "not enough free blocks"
+    assert pa.status_str(6) == "request exceeds the fixed no-allocation scratch"
     assert pa.status_str(99) == "unknown status"
     assert L.pa_abi_version() == 4
 

@@ -1,0 +1,110 @@
+"""pa_decode_noalloc (the decode for callers that cannot allocate) through the
+C ABI, against pa_decode on the same inputs: outputs bit-identical (the same
+kernels), and both within the decode tolerance of the oracle.  Two calls in a
+row share the library's fixed scratch, the second with a smaller input; a
+request beyond the scratch is refused before anything runs."""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+import harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    import paged_kv_cache_12_amd as pa
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _case(name, batch, ctx_hi, partition):
+    """A workload filled on both sides; returns what the two decodes need."""
+    import torch
+    wl = synth.WORKLOADS[name]
+    sc = synth.build_scenario(wl, batch=batch, ctx_hi=ctx_hi)
+    gs, os_ = H.GpuSide(sc), H.OracleSide(sc)
+    H.execute(sc, gs)
+    H.execute(sc, os_)
+    tab, lens = gs.cache.tables(sc.decode_seqs)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return dict(wl=wl, sc=sc, gs=gs, os=os_, tab=dev(tab), lens=dev(lens),
+                max_ctx=int(lens.max()), part=partition)
+
+
+def _both(c):
+    """pa_decode_noalloc and pa_decode on one case; returns both outputs."""
+    import torch
+    import paged_kv_cache_12_amd as pa
+    from paged_kv_cache_12_amd.manager import storage_to_torch
+    wl, gs = c["wl"], c["gs"]
+    q = storage_to_torch(c["sc"].q, wl.dtype).cuda()
+    o_na = torch.full_like(q, float("nan"))
+    o_ws = torch.full_like(q, float("nan"))
+    pa.pa_decode_noalloc(o_na, q, gs.cache.k_cache, gs.cache.v_cache, c["tab"], c["lens"],
+                         c["max_ctx"], wl.scale, c["part"])
+    pa.pa_decode(o_ws, q, gs.cache.k_cache, gs.cache.v_cache, c["tab"], c["lens"],
+                 c["max_ctx"], wl.scale, c["part"])
+    torch.cuda.synchronize()
+    return o_na, o_ws
+
+
+def _check(c, o_na, o_ws):
+    import torch
+    from test_gpu_parity import to_f64
+    wl = c["wl"]
+    assert torch.equal(o_na.view(torch.int16), o_ws.view(torch.int16)), "outputs differ"
+    rows = list(range(len(c["sc"].decode_seqs)))
+    ref = c["os"].decode(c["sc"].q, c["sc"].decode_seqs, rows)
+    return H.check_attention(to_f64(o_na, wl.dtype), ref, wl.dtype, rows)
+
+
+def test_noalloc_matches_pa_decode_twice_second_smaller():
+    import paged_kv_cache_12_amd as pa
+    # 1: long contexts, 512-token partitions: six-wave chunks and the reduce
+    big = _case("long_70b_gqa_bf16", 3, 40000, 512)
+    need = pa.pa_decode_workspace_size(3, big["wl"].h_q, big["wl"].head_dim, big["max_ctx"], 512)
+    say("noalloc call 1: long_70b_gqa_bf16 x3, max ctx", big["max_ctx"], "workspace bound", need)
+    assert 0 < need <= pa.PA_NOALLOC_SCRATCH_BYTES
+    ea, er = _check(big, *_both(big))
+    say("  bit-identical to pa_decode; max abs", ea, "max rel", er)
+    # 2: a smaller batch in 256-token partitions over the same scratch
+    small = _case("llama3_8b_gqa_bf16", 12, 1500, 256)
+    say("noalloc call 2: llama3_8b_gqa_bf16 x12, max ctx", small["max_ctx"])
+    ea, er = _check(small, *_both(small))
+    say("  bit-identical to pa_decode; max abs", ea, "max rel", er)
+    # and the first case again after the smaller one
+    ea, er = _check(big, *_both(big))
+    say("  call 1 repeated: bit-identical; max abs", ea)
+
+
+def test_noalloc_refuses_requests_beyond_its_scratch():
+    import torch
+    import paged_kv_cache_12_amd as pa
+    say("noalloc: request beyond the scratch")
+    B, H_q, H_kv, d, bs, nb = 512, 64, 8, 128, 32, 4
+    max_ctx = 131072
+    # 512 x 64 rows x 43 chunks x 520 bytes: far beyond 64 MiB
+    k = torch.zeros((nb, H_kv, d // 8, bs, 8), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((nb, H_kv, bs // 8, d, 8), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((B, H_q, d), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros_like(q)
+    tab = torch.zeros((B, max_ctx // bs), dtype=torch.int32, device="cuda")
+    lens = torch.ones(B, dtype=torch.int32, device="cuda")
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_decode_noalloc(out, q, k, v, tab, lens, max_ctx, 0.088, 512)
+    assert e.value.status == pa.PA_ERR_TOO_LARGE
+    torch.cuda.synchronize()
+    assert not torch.any(out.view(torch.int16)), "nothing may run on refusal"
