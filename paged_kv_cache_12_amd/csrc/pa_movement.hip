@@ -32,8 +32,14 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const E* __restrict__ k_n
   }
 }
 
+// Vectors each thread of copy_blocks_kernel has in flight: its loads are all
+// issued before its stores, so a copy of a few blocks takes about one memory
+// round trip instead of one per vector.
+constexpr int kCopyUnroll = 4;
+
 // grid (chunks, num_pairs, 2): z selects the K or the V cache; each thread
-// copies 16-byte vectors of one block.
+// copies kCopyUnroll 16-byte vectors of one block per round, strided by the
+// chunk grid.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ kc,
                                                           u32x4* __restrict__ vc,
                                                           const int32_t* __restrict__ pairs,
@@ -45,9 +51,21 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ kc
   u32x4* base = blockIdx.z ? vc : kc;
   const u32x4* from = base + src * vecs_per_block;
   u32x4* to = base + dst * vecs_per_block;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < vecs_per_block;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    to[i] = from[i];
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+       i0 < vecs_per_block; i0 += kCopyUnroll * stride) {
+    u32x4 x[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < vecs_per_block) x[u] = from[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < vecs_per_block) to[i] = x[u];
+    }
+  }
 }
 
 // Whole-block copies between two caches of the same geometry (device memory
@@ -192,7 +210,7 @@ PA_EXPORT pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* 
   if (num_pairs > 65535) return PA_ERR_INVALID;
   const int64_t vecs = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * e / 16;
   const int threads = 256;
-  int64_t chunks = (vecs + threads * 4 - 1) / (threads * 4);
+  int64_t chunks = (vecs + threads * kCopyUnroll - 1) / (threads * kCopyUnroll);
   if (chunks < 1) chunks = 1;
   if (chunks > 1024) chunks = 1024;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<unsigned>(chunks), num_pairs, 2),
