@@ -888,12 +888,16 @@ def run_workload(args, sc, cpu, partition):
     ceiling["pattern"] = "random 4 KiB tiles of 4 GiB, 16-byte loads, each tile once (pa_read_probe)"
     ceiling["decode_frac_of_nontemporal"] = round(unique_rate / ceiling["nontemporal_GBps"], 4)
 
-    traffic = None
+    # HBM bytes per launch from the committed counter runs (rocprofv3 passes
+    # of their own over the same command), while the decode code is the one
+    # they were taken on
+    traffic, traffic_from = None, None
     tfile = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
     if os.path.exists(tfile):
         t = json.load(open(tfile))
         if t.get("decode_source_sha256_16") == source_hash() and t.get("partition") == part:
             traffic = t.get("bytes_per_launch")
+            traffic_from = os.path.relpath(tfile, ROOT)
 
     res = {
         "metric": "paged-attn decode: effective KV HBM GB/s (% of peak) + seq-steps/sec",
@@ -927,7 +931,7 @@ def run_workload(args, sc, cpu, partition):
         # (equal to the logical bytes unless sequences share blocks)
         "roofline": {"bound": "hbm", "achieved": round(unique_rate, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(unique_rate / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
+                     "traffic": traffic, "traffic_from": traffic_from,
                      "kernel": "pa_decode" + (" (shared-prefix pass + rest + reduce)"
                                               if plan is not None else
                                               " (partition kernel + reduce)"
