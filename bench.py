@@ -42,6 +42,8 @@ SPIN_CYCLES = 2_400_000
 # run and nested in the line under its own name
 DEFAULT_WORKLOAD = "long_70b_gqa_bf16"
 DEFAULT_ALSO = "llama3_8b_gqa_bf16"
+# --swap moves half of this workload's sequences out and back
+SWAP_WORKLOAD = "llama3_8b_gqa_bf16"
 # keys of a nested workload record
 NESTED_KEYS = ("value", "unit", "ms_per_step", "pct_of_hbm_peak", "seq_steps_per_s", "dtype",
                "config", "decode_ms_mean", "decode_cold_copies",
@@ -58,7 +60,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(synth.WORKLOADS),
+                    help=f"decode workload (default {DEFAULT_WORKLOAD}; {SWAP_WORKLOAD} for --swap)")
     ap.add_argument("--also", default=None, choices=sorted(synth.WORKLOADS) + ["none"],
                     help="a second workload measured in the same run and nested in the line "
                          f"(default: {DEFAULT_ALSO} with the default --workload, else none)")
@@ -405,7 +408,7 @@ def bench_swap(args):
     import paged_kv_cache_12_amd as pa
     from oracle import attention as A
     from paged_kv_cache_12_amd.manager import PagedKVCache
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[args.workload or SWAP_WORKLOAD]
     sc = synth.build_scenario(wl)
     dev = torch.device("cuda:0")
     cache = PagedKVCache(sc.num_blocks, wl.block_size, wl.h_kv, wl.head_dim, wl.dtype,
@@ -686,8 +689,9 @@ def main():
     if args.beam:
         bench_beam(args)
         return
-    also = args.also or (DEFAULT_ALSO if args.workload == DEFAULT_WORKLOAD else "none")
-    names = [args.workload] + ([also] if also not in ("none", args.workload) else [])
+    workload = args.workload or DEFAULT_WORKLOAD
+    also = args.also or (DEFAULT_ALSO if workload == DEFAULT_WORKLOAD else "none")
+    names = [workload] + ([also] if also not in ("none", workload) else [])
     scs = {n: synth.build_scenario(synth.WORKLOADS[n]) for n in names}
     # the oracle on the host first: its workers are forked before any GPU use
     cpus = {n: None if args.no_cpu_baseline else

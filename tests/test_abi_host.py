@@ -107,6 +107,33 @@ def test_decode_validation(L):
     assert _decode(L, flags=2) == INV                  # unknown flag
 
 
+def _decode_noalloc(L, **kw):
+    a = dict(out=16, q=16, kc=16, vc=16, bt=16, maxb=8, lens=16, B=2, max_ctx=100, H_q=8,
+             H_kv=2, d=128, bs=16, nb=10, scale=0.1, part=512, dt=2, flags=0, stream=None)
+    a.update(kw)
+    return L.pa_decode_noalloc(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["maxb"], a["lens"],
+                               None, a["B"], a["max_ctx"], a["H_q"], a["H_kv"], a["d"], a["bs"],
+                               a["nb"], a["scale"], a["part"], a["dt"], a["flags"], a["stream"])
+
+
+def test_decode_noalloc_validation(L):
+    """The no-allocation decode refuses what pa_decode refuses, and a request
+    whose partials exceed its fixed scratch, all before any device call (the
+    pointers here are placeholders: every case must be refused first)."""
+    INV, UNS = pa.PA_ERR_INVALID, pa.PA_ERR_UNSUPPORTED
+    assert pa.PA_NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert _decode_noalloc(L, B=0) == pa.PA_OK
+    assert _decode_noalloc(L, part=0, H_q=6, H_kv=4) == INV
+    assert _decode_noalloc(L, part=0, d=96) == UNS
+    assert _decode_noalloc(L, part=0, dt=5) == UNS
+    assert _decode_noalloc(L, part=0, scale=0.0) == INV
+    assert _decode_noalloc(L, part=0, max_ctx=8 * 16 + 1) == INV
+    assert _decode_noalloc(L, part=0, q=None) == INV
+    # 512 x 64 rows x 43 chunks x 520 bytes of partials: beyond 64 MiB
+    big = dict(B=512, H_q=64, H_kv=8, bs=32, max_ctx=131072, maxb=4096)
+    assert _decode_noalloc(L, **big) == pa.PA_ERR_TOO_LARGE
+
+
 def test_read_probe_validation(L):
     INV = pa.PA_ERR_INVALID
     P = L.pa_read_probe

@@ -44,7 +44,7 @@ def _case(name, batch, ctx_hi, partition):
                 max_ctx=int(lens.max()), part=partition)
 
 
-def _both(c):
+def _both(c, flags=0):
     """pa_decode_noalloc and pa_decode on one case; returns both outputs."""
     import torch
     import paged_kv_cache_12_amd as pa
@@ -54,9 +54,9 @@ def _both(c):
     o_na = torch.full_like(q, float("nan"))
     o_ws = torch.full_like(q, float("nan"))
     pa.pa_decode_noalloc(o_na, q, gs.cache.k_cache, gs.cache.v_cache, c["tab"], c["lens"],
-                         c["max_ctx"], wl.scale, c["part"])
+                         c["max_ctx"], wl.scale, c["part"], flags=flags)
     pa.pa_decode(o_ws, q, gs.cache.k_cache, gs.cache.v_cache, c["tab"], c["lens"],
-                 c["max_ctx"], wl.scale, c["part"])
+                 c["max_ctx"], wl.scale, c["part"], flags=flags)
     torch.cuda.synchronize()
     return o_na, o_ws
 
@@ -65,7 +65,8 @@ def _check(c, o_na, o_ws):
     import torch
     from test_gpu_parity import to_f64
     wl = c["wl"]
-    assert torch.equal(o_na.view(torch.int16), o_ws.view(torch.int16)), "outputs differ"
+    bits = torch.int32 if wl.dtype == "f32" else torch.int16
+    assert torch.equal(o_na.view(bits), o_ws.view(bits)), "outputs differ"
     rows = list(range(len(c["sc"].decode_seqs)))
     ref = c["os"].decode(c["sc"].q, c["sc"].decode_seqs, rows)
     return H.check_attention(to_f64(o_na, wl.dtype), ref, wl.dtype, rows)
@@ -88,6 +89,20 @@ def test_noalloc_matches_pa_decode_twice_second_smaller():
     # and the first case again after the smaller one
     ea, er = _check(big, *_both(big))
     say("  call 1 repeated: bit-identical; max abs", ea)
+
+
+@pytest.mark.parametrize("name,batch,ctx_hi,part", [("tiny_mha_fp32", None, None, 64),
+                                                     ("opt13b_sampling_cow_fp16", 16, 300, 128)])
+def test_noalloc_fp32_and_fp16(name, batch, ctx_hi, part):
+    """The fp32 path (one slot per partition) and fp16 over blocks shared by
+    forked samples (cached loads), each twice in a row on the same scratch."""
+    import paged_kv_cache_12_amd as pa
+    c = _case(name, batch, ctx_hi, part)
+    flags = pa.PA_DECODE_SHARED_KV if c["gs"].pool.stats()["shared"] > 0 else 0
+    say("noalloc:", name, "partition", part, "max ctx", c["max_ctx"], "flags", flags)
+    for _ in range(2):
+        ea, er = _check(c, *_both(c, flags))
+    say("  bit-identical to pa_decode; max abs", ea, "max rel", er)
 
 
 def test_noalloc_refuses_requests_beyond_its_scratch():
