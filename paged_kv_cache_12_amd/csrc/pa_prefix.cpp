@@ -31,7 +31,10 @@
 namespace pa {
 
 // ---------------------------------------------------------------------------
-// SHA-256 (FIPS 180-4)
+// SHA-256 (FIPS 180-4).  kK is the standard's table of 64 round constants
+// (section 4.2.2) and the initial hash value below is its section 5.3.3;
+// both are data of the published algorithm, taken from the standard (the
+// initial value is in the Sha256 constructor below).
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -80,9 +83,11 @@ void compress_portable(uint32_t h[8], const uint8_t* m, size_t nblocks) {
   }
 }
 
-// The same with the x86 SHA extensions: the state lives as (A,B,E,F) and
-// (C,D,G,H); each sha256rnds2 does two rounds, sha256msg1/msg2 extend the
-// message schedule four words at a time.
+// The same with the x86 SHA extensions, following the published method of
+// Intel's "Intel SHA Extensions" paper (Gulley et al., 2013): the state lives
+// as (A,B,E,F) and (C,D,G,H), the register packing sha256rnds2 requires; each
+// sha256rnds2 does two rounds, sha256msg1/msg2 extend the message schedule
+// four words at a time.
 __attribute__((target("sha,sse4.1,ssse3"))) void compress_shani(uint32_t h[8],
                                                                 const uint8_t* m,
                                                                 size_t nblocks) {
