@@ -228,6 +228,9 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * that the library holds on each GPU it runs on until the process ends.  The
  * array's address is looked up once per device, on the first call that needs
  * it with that device current; nothing is allocated or freed, here or later.
+ * Make that first call outside graph capture; later calls may be captured
+ * into a HIP graph and replayed (the kernels read their inputs and write the
+ * array and out at the addresses given at capture).
  *
  * Limit: the call's partials, num_seqs x num_q_heads x slots x
  * (4 x head_dim + 8) bytes with one slot per chunk of partitions that a row

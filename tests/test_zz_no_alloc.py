@@ -105,6 +105,53 @@ def test_noalloc_fp32_and_fp16(name, batch, ctx_hi, part):
     say("  bit-identical to pa_decode; max abs", ea, "max rel", er)
 
 
+def test_noalloc_under_graph_capture():
+    """The caller it exists for: a decode captured into a HIP graph (torch's
+    CUDAGraph) and replayed.  Each replay, with eager work and
+    synchronisations between replays, matches the eager call bit for bit;
+    after new query values are written in place, a replay matches an eager
+    call on them.  One eager call comes first: it looks up the scratch
+    address on this device, a call that is not made under capture."""
+    import torch
+    import paged_kv_cache_12_amd as pa
+    from paged_kv_cache_12_amd.manager import storage_to_torch
+    c = _case("llama3_8b_gqa_bf16", 12, 1500, 256)
+    wl, gs = c["wl"], c["gs"]
+    say("noalloc under graph capture: llama3_8b_gqa_bf16 x12, partition 256")
+    q = storage_to_torch(c["sc"].q, wl.dtype).cuda()
+    args = (gs.cache.k_cache, gs.cache.v_cache, c["tab"], c["lens"], c["max_ctx"], wl.scale,
+            c["part"])
+    o_eager = torch.empty_like(q)
+    pa.pa_decode_noalloc(o_eager, q, *args)
+    torch.cuda.synchronize()
+    o_graph = torch.full_like(q, float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pa.pa_decode_noalloc(o_graph, q, *args)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    o_other = torch.empty_like(q)
+    for r in range(3):
+        o_graph.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_graph.view(torch.int16), o_eager.view(torch.int16)), f"replay {r}"
+        # eager work on the same scratch between replays
+        pa.pa_decode_noalloc(o_other, q, *args)
+        torch.cuda.synchronize()
+    q.mul_(-0.5)
+    pa.pa_decode_noalloc(o_eager, q, *args)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(o_graph.view(torch.int16), o_eager.view(torch.int16)), "replay on new q"
+    ea, er = _check(c, *_both(c))
+    say("  replays bit-identical to eager calls")
+
+
 def test_noalloc_refuses_requests_beyond_its_scratch():
     import torch
     import paged_kv_cache_12_amd as pa
