@@ -48,7 +48,7 @@ SWAP_WORKLOAD = "llama3_8b_gqa_bf16"
 NESTED_KEYS = ("value", "unit", "ms_per_step", "pct_of_hbm_peak", "seq_steps_per_s", "dtype",
                "config", "decode_ms_mean", "decode_cold_copies",
                "decode_ms_per_call_p10_median_p90", "host_us_per_step", "copy_blocks",
-               "roofline", "read_ceiling", "cpu_baseline")
+               "roofline", "read_ceiling", "kv_memory", "cpu_baseline")
 # the decode kernels' code: their source and the library headers with device
 # code or structures they use (the public header only declares the ABI)
 DECODE_SRC = [os.path.join(ROOT, "paged_kv_cache_12_amd", "csrc", f)
@@ -266,6 +266,24 @@ def unique_kv_bytes(tables, lens, wl):
             fill = min(bs, int(n) - j * bs)
             seen[b] = max(seen.get(b, 0), fill)
     return float(sum(seen.values())) * 2 * wl.h_kv * wl.head_dim * synth.ELEM_BYTES[wl.dtype]
+
+
+def kv_memory(used_blocks: int, block_size: int, unique_bytes: float, logical_bytes: float,
+              lens, token_bytes: int) -> dict:
+    """KV memory of the batch as the pool holds it, beside a contiguous
+    allocator that reserves the longest context for every sequence (the
+    pre-paging systems the pages describe reserve the maximum length per
+    request and cannot share a prefix).  Fractions of reserved slots that
+    hold a token."""
+    slots = int(used_blocks) * block_size
+    distinct = unique_bytes / token_bytes
+    logical = logical_bytes / token_bytes
+    reserved = len(lens) * int(max(lens)) if len(lens) else 0
+    return {"paged_slots": slots, "paged_tokens_distinct": round(distinct),
+            "paged_used_frac": round(distinct / slots, 4) if slots else None,
+            "contiguous_slots": reserved, "contiguous_tokens": round(logical),
+            "contiguous_used_frac": round(logical / reserved, 4) if reserved else None,
+            "paged_bytes": slots * token_bytes, "contiguous_bytes": reserved * token_bytes}
 
 
 def host_cores() -> int:
@@ -947,6 +965,8 @@ def run_workload(args, sc, cpu, partition):
                      "logical_bytes_per_launch": round(kv_dec),
                      "logical_achieved": round(achieved, 1)},
         "read_ceiling": ceiling,
+        "kv_memory": kv_memory(cache.pool.stats()["used"], wl.block_size, unique, kv_dec, len_h,
+                               2 * wl.h_kv * wl.head_dim * e),
     }
     if cpu is not None:
         res["cpu_baseline"] = cpu

@@ -84,3 +84,18 @@ def test_cpu_baseline_workers_end_normally():
     res = bench.cpu_baseline(sc, 0.2, 3)
     assert res["kind"] == "oracle" and res["cores"] == 3 and res["value"] > 0
     assert bench.WORKER_EXIT_CODES == [0, 0, 0]
+
+
+def test_kv_memory_against_hand_worked_numbers():
+    """Two sequences of 60 and 17 tokens in blocks of 16 (the pages' 60-token
+    example: four blocks, the last one part full), 8 bytes per token: the
+    pool holds 6 blocks = 96 slots for 77 tokens; a contiguous allocator
+    sized to the longest sequence reserves 2 x 60 = 120 slots."""
+    km = _bench().kv_memory(6, 16, 77 * 8.0, 77 * 8.0, [60, 17], 8)
+    assert km["paged_slots"] == 96 and km["paged_tokens_distinct"] == 77
+    assert km["paged_used_frac"] == round(77 / 96, 4)
+    assert km["contiguous_slots"] == 120 and km["contiguous_used_frac"] == round(77 / 120, 4)
+    assert km["paged_bytes"] == 768 and km["contiguous_bytes"] == 960
+    # a shared prefix is stored once by the pool, once per sequence contiguously
+    km = _bench().kv_memory(3, 16, 40 * 8.0, 80 * 8.0, [40, 40], 8)
+    assert km["paged_tokens_distinct"] == 40 and km["contiguous_tokens"] == 80
