@@ -99,3 +99,36 @@ def test_kv_memory_against_hand_worked_numbers():
     # a shared prefix is stored once by the pool, once per sequence contiguously
     km = _bench().kv_memory(3, 16, 40 * 8.0, 80 * 8.0, [40, 40], 8)
     assert km["paged_tokens_distinct"] == 40 and km["contiguous_tokens"] == 80
+
+
+def test_default_line_nests_the_llama_class_record(monkeypatch, capsys):
+    """The default run measures the long-context workload and nests the
+    Llama-class record (value, step time, roofline, CPU baseline, ...) in
+    the same JSON line; --workload alone measures that workload only.  The
+    GPU parts are stood in for by records that name their workload."""
+    import json
+    bench = _bench()
+    calls = []
+
+    def fake_run(args, sc, cpu, partition):
+        calls.append(sc.wl.name)
+        rec = {k: f"{sc.wl.name}:{k}" for k in bench.NESTED_KEYS}
+        rec.update(metric="m", config={"workload": sc.wl.name}, cpu_baseline=cpu)
+        return rec
+
+    monkeypatch.setattr(bench, "run_workload", fake_run)
+    monkeypatch.setattr(bench, "cpu_baseline", lambda sc, s, w: {"sample": sc.wl.name})
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "2", "--warmup", "1"])
+    bench.main()
+    line = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert calls == ["long_70b_gqa_bf16", "llama3_8b_gqa_bf16"]
+    assert line["config"]["workload"] == "long_70b_gqa_bf16"
+    nested = line["llama3_8b_gqa_bf16"]
+    assert set(nested) == set(bench.NESTED_KEYS)
+    assert nested["roofline"] == "llama3_8b_gqa_bf16:roofline"
+    assert nested["cpu_baseline"] == {"sample": "llama3_8b_gqa_bf16"}
+    calls.clear()
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--workload", "shared_prefix_bf16"])
+    bench.main()
+    line = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert calls == ["shared_prefix_bf16"] and "llama3_8b_gqa_bf16" not in line
