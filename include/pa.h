@@ -300,6 +300,11 @@ pa_status pa_decode_order(const int32_t* block_tables, int max_blocks_per_seq,
  * (num_groups == 0 is plain pa_decode) and its three host values; max_rest
  * must be at least the largest context_lens[s] - prefix_len[s] (the reduce
  * runs only when that part spans several work-groups' worth of partitions).
+ * A plan may also be built by hand: every member of a group must hold the
+ * group's first member's blocks for its first L tokens, L <= its context, and
+ * prefix_len[s] must equal its group's L (0 outside groups).  An L that is
+ * not a multiple of 32 is taken rounded down to one; the tokens cut off run
+ * with the rest of each context.
  * Groups of at most 16 / G members run one 16-column tile per load, larger
  * ones two.  fp32 runs the plain path.  The workspace must hold
  * pa_decode_cascade_workspace_size(...) bytes, which is non-zero even for an

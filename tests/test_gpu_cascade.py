@@ -125,6 +125,50 @@ def test_cascade_decode_matches_oracle(name, part):
     assert torch.equal(again.view(torch.int16), out.view(torch.int16))
 
 
+@pytest.mark.parametrize("name,part,cut", [("prefix_g4", 512, 7), ("prefix_g4", 0, 31),
+                                           ("prefix_g4", 64, 1), ("prefix_g16", 256, 13),
+                                           ("prefix_g2_f16", 128, 5)])
+def test_cascade_prefix_length_off_the_32_grid(name, part, cut):
+    """A hand-made plan whose prefix lengths are not multiples of 32 (the
+    planner rounds down to 32, the cascade entry point takes any shared run):
+    the prefix pass ends in a part group and the rest starts inside one."""
+    import torch
+    import paged_kv_cache_12_amd as pa
+    from paged_kv_cache_12_amd.manager import storage_to_torch
+    from test_gpu_parity import to_f64
+    wl, kw = _workload(name)
+    say("cascade off-grid prefix", name, part, cut)
+    sc = synth.build_scenario(wl, **kw)
+    gs, os_ = H.GpuSide(sc), H.OracleSide(sc)
+    H.execute(sc, gs)
+    H.execute(sc, os_)
+    seqs = sc.decode_seqs
+    tab, lens = gs.cache.tables(seqs)
+    pre, groups, members, mp, mm, mr = pa.pa_cascade_plan(tab, lens, wl.block_size, wl.h_q,
+                                                          wl.h_kv, 64)
+    assert len(groups) > 0 and mp > cut
+    groups = groups.copy()
+    groups[:, 2] -= cut
+    pre = np.where(pre > 0, pre - cut, 0).astype(np.int32)
+    mp = int(groups[:, 2].max())
+    mr = int((lens - pre).max())
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q = storage_to_torch(sc.q, wl.dtype).cuda()
+    max_ctx = int(lens.max())
+    ws = torch.zeros(max(256, pa.pa_decode_cascade_workspace_size(len(seqs), wl.h_q, wl.head_dim,
+                                                                  max_ctx, part)),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    pa.pa_decode_cascade(out, q, gs.cache.k_cache, gs.cache.v_cache, dev(tab), dev(lens), max_ctx,
+                         wl.scale, part, dev(pre), dev(groups.reshape(-1)), dev(members), mp, mm, mr,
+                         ws, flags=pa.PA_DECODE_SHARED_KV)
+    torch.cuda.synchronize()
+    rows = list(range(len(seqs)))
+    ref = os_.decode(sc.q, seqs, rows)
+    ea, _ = H.check_attention(to_f64(out, wl.dtype), ref, wl.dtype, rows)
+    say("  groups", len(groups), "prefix", mp, "max abs", ea)
+
+
 def test_cascade_with_no_groups_is_plain_decode():
     import torch
     import paged_kv_cache_12_amd as pa
