@@ -736,239 +736,6 @@ void decode_part_mfma(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Shared-prefix pass on 32x32x16 matrix cores: one 32-column tile per wave.
-//
-// The columns are those of the two-tile form above (column c: member c / G,
-// query head c % G, up to 32 / G members), but a 32-token group takes D / 16
-// QK and D / 16 PV instructions of the 32x32x16 shape where two 16-column
-// tiles take four times as many of the 16x16x32 shape (half the work each),
-// and its softmax runs once over 16 scores per lane.
-//
-// Lane layouts (v_mfma_f32_32x32x16): A operand row l % 32, k = 8(l / 32) + i;
-// B operand column l % 32, the same k; C register r of lane l holds row
-// 8(r / 4) + 4(l / 32) + r % 4, column l % 32.  Score row i of a group holds
-// token pi(i), i with bits 2 and 3 exchanged, so register r of lane l is
-// token 16(r / 8) + 8(l / 32) + r % 8: registers 0-7 and 8-15 are the PV B
-// operand over tokens 0-15 and 16-31 with eight consecutive tokens per lane,
-// the tokens of one 16-byte V slab.
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-template <typename T>
-struct Mfma32;
-
-template <>
-struct Mfma32<__bf16> {
-  static __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct Mfma32<_Float16> {
-  static __device__ __forceinline__ f32x16 mma(f16x8 a, f16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-};
-
-// One 32-token group's operands: K[kk] = dims 16kk + 8(l / 32) .. +8 of score
-// row l % 32's token; V[jt][ks] = dim 32jt + l % 32 of tokens
-// 16ks + 8(l / 32) .. +8.
-template <typename T, int D>
-struct WideTiles {
-  typedef typename Mfma<T>::v8 v8;
-  v8 k[D / 16];
-  v8 v[D / 32][2];
-};
-
-template <typename T, int D, int BS, bool NT>
-__device__ __forceinline__ void load_wide(WideTiles<T, D>& W, TableWindow& w,
-                                          const int32_t* __restrict__ bt, int tg, int nb_valid,
-                                          int num_blocks, const T* kh, const T* vh,
-                                          int64_t blk_stride, int kblk, int krow, int half,
-                                          int lane) {
-  typedef typename Mfma<T>::v8 v8;
-  constexpr int BPT = 32 / BS;
-  const int lb0 = tg / BS;
-  if (lb0 + BPT - 1 >= w.lb_base + 64) fill_window(w, bt, lb0, nb_valid, num_blocks, lane);
-  int64_t boff[BPT];
-#pragma unroll
-  for (int j = 0; j < BPT; ++j)
-    boff[j] = static_cast<int64_t>(__builtin_amdgcn_readlane(w.ids, lb0 + j - w.lb_base)) *
-              blk_stride;
-  const T* kbase = kh + boff[kblk] + krow * 8;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    W.k[kk] = load16<v8, NT>(kbase + (2 * kk + half) * (BS * 8));
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int t8 = 16 * ks + 8 * half;  // first token of this lane's V slab
-    const T* vbase = vh + boff[t8 / BS] + ((t8 % BS) / 8) * (D * 8) + (lane & 31) * 8;
-#pragma unroll
-    for (int jt = 0; jt < D / 32; ++jt) W.v[jt][ks] = load16<v8, NT>(vbase + 32 * jt * 8);
-  }
-}
-
-// QK, online softmax and PV for one whole 32-token group.
-template <typename T, int D>
-__device__ __forceinline__ void compute_wide(const WideTiles<T, D>& W,
-                                             const typename Mfma<T>::v8* qop, f32x16* o,
-                                             float& m, float& l, int half, float scale_log2) {
-  typedef typename Mfma<T>::v8 v8;
-  f32x16 s;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) s = Mfma32<T>::mma(W.k[kk], qop[kk], s);
-  float x[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) x[r] = s[r];
-  float mx[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) mx[i] = fmaxf(x[i], x[i + 8]);
-  const float mraw = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])),
-                           fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
-  const float mloc = mraw * scale_log2;  // scale > 0: the max commutes with it
-  // lazy rescale, as in qk_softmax; a column's two token halves sit in lanes
-  // l and l ^ 32
-  if (__builtin_amdgcn_ballot_w64(mloc > m + kRescaleLog2)) {
-    __asm__ volatile("");  // keep the path a real branch (not speculated)
-    const float mnew = fmaxf(m, xor_max(mloc, 32));
-    const float alpha = fast_exp2(m - mnew);
-    l *= alpha;
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) o[j] *= alpha;
-    m = mnew;
-  }
-  float psum = 0.f;
-  v8 pop[2];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float e = fast_exp2(fmaf(x[r], scale_log2, -m));
-    psum += e;
-    pop[r >> 3][r & 7] = static_cast<T>(e);
-  }
-  l += psum;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int jt = 0; jt < D / 32; ++jt) o[jt] = Mfma32<T>::mma(W.v[jt][ks], pop[ks], o[jt]);
-}
-
-// Work decomposition as kPrefix2 of decode_part_mfma: one work-group per
-// (chunk, KV head, column group), NW waves over the chunk's partitions, one
-// merge round in LDS, partials only.
-template <typename T, int D, int BS, int NW, bool NT>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_prefix_wide(float* __restrict__ ws_o, float2* __restrict__ ws_ml,
-                        const T* __restrict__ q, const T* kc, const T* vc,
-                        const int32_t* __restrict__ block_tables, int maxb, int H_q, int H_kv,
-                        int G, int n_hg, int num_blocks, float scale_log2, int part, int maxC,
-                        int ws_stride, Cascade cas) {
-  typedef typename Mfma<T>::v8 v8;
-  constexpr int NK = D / 16, NO = D / 32;
-  constexpr int TILE = BS * D;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 31;
-  const int half = lane >> 5;
-  const WorkItem wi = work_item<!NT>(blockIdx.x, H_kv * n_hg, cas.ngroups, maxC);
-  const int ch = wi.chunk;
-  const int kvh = wi.hgl / n_hg;
-  const int gi = wi.seq;
-  const int first = cas.groups[3 * gi], count = cas.groups[3 * gi + 1];
-  const int hi = prefix_tokens(cas.groups[3 * gi + 2], INT_MAX);
-  const int s = cas.members[first];
-  const int mi = col / G;
-  const int hin = col - mi * G;
-  const bool hvalid = mi < count;
-  const int s_col = hvalid ? cas.members[first + mi] : s;
-
-  const ChunkSpan sp = range_span<NW>(0, hi, part, ch, wave);
-  if (ch >= sp.nchunks) return;  // uniform over the work-group
-  const int t0 = sp.t0, t1 = sp.t1;
-
-  // B operand of QK: Q[column][dims 16kk + 8 half .. +8]
-  v8 qop[NK];
-  {
-    const T* qrow = q + (static_cast<int64_t>(s_col) * H_q + kvh * G + hin) * D + 8 * half;
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) qop[kk] = *reinterpret_cast<const v8*>(qrow + 16 * kk);
-  }
-  f32x16 o[NO];
-#pragma unroll
-  for (int j = 0; j < NO; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
-  float m = -INFINITY, l = 0.f;
-
-  const int32_t* bt = block_tables + static_cast<int64_t>(s) * maxb;
-  const int64_t blk_stride = static_cast<int64_t>(H_kv) * TILE;
-  const T* kh = kc + static_cast<int64_t>(kvh) * TILE;
-  const T* vh = vc + static_cast<int64_t>(kvh) * TILE;
-  // this lane's K row: token pi(col) of the group
-  const int u = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
-  const int kblk = u / BS;
-  const int krow = k_row<BS>(u % BS);
-
-  // hi and the partition size are multiples of 32, and so is every range
-  // boundary: whole groups only
-  const int nb_valid = t1 / BS;
-  TableWindow win;
-  fill_window(win, bt, t0 / BS, nb_valid, num_blocks, lane);
-  for (int tg = t0; tg < t1; tg += 32) {
-    WideTiles<T, D> W;
-    load_wide<T, D, BS, NT>(W, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
-                            half, lane);
-    compute_wide<T, D>(W, qop, o, m, l, half, scale_log2);
-  }
-  const float lt = xor_sum(l, 32);
-
-  // One merge round: every wave's (m, l, o) goes to LDS; after one barrier
-  // each wave combines the NW states for its share of the (32-dim tile,
-  // register quad) slices with weights 2^(m_w - M) and writes them.
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  __shared__ float all_m[NW][32];
-  __shared__ float all_l[NW][32];
-  __shared__ f32x4 all_o[NW][NO * 4][64];
-  if (half == 0) {
-    all_m[wave][col] = m;
-    all_l[wave][col] = lt;
-  }
-#pragma unroll
-  for (int j = 0; j < NO; ++j)
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd)
-      all_o[wave][4 * j + qd][lane] =
-          f32x4{o[j][4 * qd], o[j][4 * qd + 1], o[j][4 * qd + 2], o[j][4 * qd + 3]};
-  __syncthreads();
-  if (!hvalid) return;  // no barrier follows
-  const int64_t slot =
-      (static_cast<int64_t>(s_col) * H_q + kvh * G + hin) * ws_stride + ch;
-  for (int pi = wave; pi < NO * 4; pi += NW) {  // uniform over the wave
-    float mw[NW];
-    float mm = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      mw[w] = all_m[w][col];
-      mm = fmaxf(mm, mw[w]);
-    }
-    float ls = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - mm);
-      ls = fmaf(f, all_l[w][col], ls);
-      acc += f * all_o[w][pi][lane];
-    }
-    // slice pi: dims 32(pi / 4) + 8(pi % 4) + 4 half .. +4
-    const int dim = 32 * (pi >> 2) + 8 * (pi & 3) + 4 * half;
-    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(ws_o + slot * D + dim));
-    if (pi == 0 && half == 0)
-      __builtin_nontemporal_store(f32x2{mm, ls}, reinterpret_cast<f32x2*>(ws_ml + slot));
-  }
-}
-
 // fp32 path: one wavefront per (partition, query head, sequence).  QK: lane t
 // (< BS) owns token t of the block; PV: lane owns dims lane and lane + 64.
 template <int D, int BS>
@@ -1214,18 +981,6 @@ void launch_part(const DecodeArgs& a, int maxC, int ws_stride, int nitems) {
                      a.scale_log2, a.part, maxC, ws_stride, a.cas, a.nkv);
 }
 
-template <typename T, int D, int BS, int NW, bool NT>
-void launch_wide(const DecodeArgs& a, int maxC, int ws_stride) {
-  const int n_hg = (a.G + 15) / 16;
-  const int64_t grid = static_cast<int64_t>(maxC) * a.H_kv * n_hg * a.cas.ngroups;
-  if (grid == 0) return;
-  hipLaunchKernelGGL((decode_prefix_wide<T, D, BS, NW, NT>), dim3(static_cast<unsigned>(grid)),
-                     dim3(64 * NW), 0, a.st, a.ws_o, a.ws_ml, static_cast<const T*>(a.q),
-                     static_cast<const T*>(a.kc), static_cast<const T*>(a.vc), a.bt, a.maxb,
-                     a.H_q, a.H_kv, a.G, n_hg, a.num_blocks, a.scale_log2, a.part, maxC,
-                     ws_stride, a.cas);
-}
-
 // Partial slots per (sequence, query head) row.
 inline int host_chunks(int n, int part, int nw) {
   if (part <= 0) return 1;
@@ -1266,9 +1021,9 @@ void launch_mfma_nw(const DecodeArgs& a) {
   const bool reread = a.max_members >= 32 / a.G;
   if (two) {
     if (reread)
-      launch_wide<T, D, BS, NWP2, false>(b, cp, stride);
+      launch_part<T, D, BS, NWP2, false, kPrefix2>(b, cp, stride, a.cas.ngroups);
     else
-      launch_wide<T, D, BS, NWP2, true>(b, cp, stride);
+      launch_part<T, D, BS, NWP2, true, kPrefix2>(b, cp, stride, a.cas.ngroups);
   } else {
     if (reread)
       launch_part<T, D, BS, NWP, false, kPrefix>(b, cp, stride, a.cas.ngroups);
