@@ -736,8 +736,45 @@ void decode_part_mfma(
   }
 }
 
-// fp32 path: one wavefront per (partition, query head, sequence).  QK: lane t
-// (< BS) owns token t of the block; PV: lane owns dims lane and lane + 64.
+// fp32 path: one wavefront per (partition, query head, sequence).  QK: the
+// TPL = 64 / BS lanes of token t (lanes t*TPL ..) each take D / TPL of its
+// dims and add their dot products by shuffles; PV: lane owns dims lane and
+// lane + 64.  The block table comes in 64-entry windows (one entry per lane),
+// and (F32Tile::PREFETCH) the next block's K and V are requested before this
+// block's arithmetic, so that the loop does not wait a memory round trip per
+// block.
+template <int D, int BS>
+struct F32Tile {
+  static constexpr int X = 4;              // fp32 elements per 16-byte vector
+  static constexpr int TPL = 64 / BS;      // QK lanes per token
+  static constexpr int NK = D / TPL / X;   // K vectors per lane
+  static constexpr int DPL = D / 64;       // PV dims per lane
+  static constexpr int NV = BS / X * DPL;  // V vectors per lane
+  // the next tile is requested ahead when two tiles leave room for two waves
+  // per SIMD (head_dim 128 with 32-token blocks would hold 256 registers)
+  static constexpr bool PREFETCH = NK + NV <= 16;
+  f32x4 k[NK];
+  f32x4 v[NV];
+};
+
+template <int D, int BS>
+__device__ __forceinline__ void load_f32_tile(F32Tile<D, BS>& T, const float* kt,
+                                              const float* vt, int tok, int quarter, int lane) {
+  typedef F32Tile<D, BS> F;
+  // K [D/X][BS][X]: the lane's dims 4j .. 4j+3 of token tok, j = quarter*NK + u
+#pragma unroll
+  for (int u = 0; u < F::NK; ++u)
+    T.k[u] = *reinterpret_cast<const f32x4*>(
+        kt + ((quarter * F::NK + u) * BS + k_row<BS>(tok)) * F::X);
+  // V [BS/X][D][X]: tokens 4t4 .. 4t4+3 of dim lane + 64k
+#pragma unroll
+  for (int t4 = 0; t4 < BS / F::X; ++t4)
+#pragma unroll
+    for (int k = 0; k < F::DPL; ++k)
+      T.v[t4 * F::DPL + k] =
+          *reinterpret_cast<const f32x4*>(vt + (t4 * D + lane + 64 * k) * F::X);
+}
+
 template <int D, int BS>
 __global__ __launch_bounds__(64) void decode_part_f32(
     float* __restrict__ out, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
@@ -745,85 +782,115 @@ __global__ __launch_bounds__(64) void decode_part_f32(
     const int32_t* __restrict__ block_tables, int maxb, const int32_t* __restrict__ ctx_lens,
     int max_tokens, int H_q, int H_kv, int G, int num_blocks, float scale_log2, int part,
     int maxP) {
-  constexpr int X = 4;
-  constexpr int DPL = D / 64;
+  typedef F32Tile<D, BS> F;
   constexpr int TILE = BS * D;
   const int lane = threadIdx.x;
   const int p = blockIdx.x;
   const int qh = blockIdx.y;
   const int s = blockIdx.z;
   const int kvh = qh / G;
+  const int tok = lane / F::TPL, quarter = lane % F::TPL;
 
   const Span sp = partition_span(ctx_lens, s, max_tokens, part, p);
   if (p >= sp.nparts) return;
   const int t0 = sp.t0, t1 = sp.t1;
 
-  __shared__ float qs[D];
+  // this lane's share of q: dims 4j .. 4j+3, j = quarter*NK + u
   const int64_t row = static_cast<int64_t>(s) * H_q + qh;
-  for (int i = lane; i < D; i += 64) qs[i] = q[row * D + i];
-  __syncthreads();
-
-  float acc[DPL];
+  f32x4 qv[F::NK];
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+  for (int u = 0; u < F::NK; ++u)
+    qv[u] = *reinterpret_cast<const f32x4*>(q + row * D + (quarter * F::NK + u) * F::X);
+
+  float acc[F::DPL];
+#pragma unroll
+  for (int k = 0; k < F::DPL; ++k) acc[k] = 0.f;
   float m = -INFINITY, l = 0.f;
   const int32_t* bt = block_tables + static_cast<int64_t>(s) * maxb;
+  const int lb_end = (t1 + BS - 1) / BS;
+  const int64_t head_off = static_cast<int64_t>(kvh) * TILE;
+  const int64_t blk_stride = static_cast<int64_t>(H_kv) * TILE;
 
-  for (int lb = t0 / BS; lb * BS < t1; ++lb) {
-    int b = bt[lb];
-    if (b < 0 || b >= num_blocks) b = 0;
-    const float* kt = kc + (static_cast<int64_t>(b) * H_kv + kvh) * TILE;
-    const float* vt = vc + (static_cast<int64_t>(b) * H_kv + kvh) * TILE;
-    const int nval = (t1 - lb * BS) < BS ? (t1 - lb * BS) : BS;
-    float sc = -INFINITY;
-    if (lane < BS) {
-      float dot = 0.f;
-#pragma unroll 4
-      for (int j = 0; j < D / X; ++j) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(kt + (j * BS + k_row<BS>(lane)) * X);
-        dot = fmaf(qs[4 * j + 0], kv[0], dot);
-        dot = fmaf(qs[4 * j + 1], kv[1], dot);
-        dot = fmaf(qs[4 * j + 2], kv[2], dot);
-        dot = fmaf(qs[4 * j + 3], kv[3], dot);
-      }
-      if (lane < nval) sc = dot * scale_log2;
+  TableWindow win;
+  int lb = t0 / BS;
+  if (lb < lb_end) {
+    fill_window(win, bt, lb, lb_end, num_blocks, lane);
+    F32Tile<D, BS> cur;
+    if constexpr (F::PREFETCH) {
+      const int64_t o = static_cast<int64_t>(__builtin_amdgcn_readlane(win.ids, 0)) * blk_stride;
+      load_f32_tile<D, BS>(cur, kc + o + head_off, vc + o + head_off, tok, quarter, lane);
     }
-    float bm = sc;
+    for (; lb < lb_end; ++lb) {
+      F32Tile<D, BS> nxt;
+      if constexpr (F::PREFETCH) {
+        // request the next block before this block's arithmetic
+        if (lb + 1 < lb_end) {
+          if (lb + 1 >= win.lb_base + 64) fill_window(win, bt, lb + 1, lb_end, num_blocks, lane);
+          const int64_t o =
+              static_cast<int64_t>(__builtin_amdgcn_readlane(win.ids, lb + 1 - win.lb_base)) *
+              blk_stride;
+          load_f32_tile<D, BS>(nxt, kc + o + head_off, vc + o + head_off, tok, quarter, lane);
+        }
+      } else {
+        if (lb >= win.lb_base + 64) fill_window(win, bt, lb, lb_end, num_blocks, lane);
+        const int64_t o =
+            static_cast<int64_t>(__builtin_amdgcn_readlane(win.ids, lb - win.lb_base)) *
+            blk_stride;
+        load_f32_tile<D, BS>(cur, kc + o + head_off, vc + o + head_off, tok, quarter, lane);
+      }
+      const int nval = (t1 - lb * BS) < BS ? (t1 - lb * BS) : BS;
+      float dot = 0.f;
 #pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) bm = xor_max(bm, mask);
-    const float mnew = fmaxf(m, bm);
-    const float alpha = fast_exp2(m - mnew);
-    const float pe = (lane < nval) ? fast_exp2(sc - mnew) : 0.f;
-    float ps = pe;
+      for (int u = 0; u < F::NK; ++u) {
+        dot = fmaf(qv[u][0], cur.k[u][0], dot);
+        dot = fmaf(qv[u][1], cur.k[u][1], dot);
+        dot = fmaf(qv[u][2], cur.k[u][2], dot);
+        dot = fmaf(qv[u][3], cur.k[u][3], dot);
+      }
 #pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) ps = xor_sum(ps, mask);
-    l = l * alpha + ps;
-    m = mnew;
+      for (int mask = 1; mask < F::TPL; mask <<= 1) dot = xor_sum(dot, mask);
+      const float sc = tok < nval ? dot * scale_log2 : -INFINITY;
+      float bm = sc;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) acc[k] *= alpha;
+      for (int mask = 32; mask >= 1; mask >>= 1) bm = xor_max(bm, mask);
+      const float mnew = fmaxf(m, bm);
+      const float alpha = fast_exp2(m - mnew);
+      const float pe = tok < nval ? fast_exp2(sc - mnew) : 0.f;
+      // each token once: the first of its lanes
+      float ps = quarter == 0 ? pe : 0.f;
 #pragma unroll
-    for (int t4 = 0; t4 < BS / X; ++t4) {
+      for (int mask = 32; mask >= 1; mask >>= 1) ps = xor_sum(ps, mask);
+      l = l * alpha + ps;
+      m = mnew;
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) {
-        const f32x4 vv =
-            *reinterpret_cast<const f32x4*>(vt + (t4 * D + lane + 64 * k) * X);
+      for (int k = 0; k < F::DPL; ++k) acc[k] *= alpha;
 #pragma unroll
-        for (int e = 0; e < X; ++e) {
-          const int t = t4 * X + e;
-          const float pt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), t));
-          if (t < nval) acc[k] = fmaf(pt, vv[e], acc[k]);
+      for (int t4 = 0; t4 < BS / F::X; ++t4) {
+#pragma unroll
+        for (int e = 0; e < F::X; ++e) {
+          const int t = t4 * F::X + e;
+          const float pt =
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), t * F::TPL));
+          // tokens past the fill: weight 0, and the slot's V may hold anything
+          if (t < nval) {
+#pragma unroll
+            for (int k = 0; k < F::DPL; ++k)
+              acc[k] = fmaf(pt, cur.v[t4 * F::DPL + k][e], acc[k]);
+          }
         }
       }
+      if constexpr (F::PREFETCH)
+        if (lb + 1 < lb_end) cur = nxt;
     }
   }
   if (sp.nparts == 1) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) out[row * D + lane + 64 * k] = acc[k] * inv;
+    for (int k = 0; k < F::DPL; ++k) out[row * D + lane + 64 * k] = acc[k] * inv;
   } else {
     float* dst = ws_o + (row * maxP + p) * D;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) dst[lane + 64 * k] = acc[k];
+    for (int k = 0; k < F::DPL; ++k) dst[lane + 64 * k] = acc[k];
     if (lane == 0) ws_ml[row * maxP + p] = make_float2(m, l);
   }
 }

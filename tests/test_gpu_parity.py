@@ -183,7 +183,7 @@ def run_both(sc, partition, rows=None, guard=1):
 
 @pytest.mark.parametrize("dtype,h_q,h_kv,d,bs,part", [
     ("f32", 4, 4, 64, 16, 0), ("f32", 4, 4, 64, 16, 32), ("f32", 8, 2, 128, 32, 64),
-    ("f32", 6, 3, 64, 32, 512),
+    ("f32", 6, 3, 64, 32, 512), ("f32", 4, 2, 128, 16, 0),
     ("bf16", 32, 8, 128, 16, 512), ("bf16", 32, 8, 128, 16, 0), ("bf16", 32, 8, 128, 16, 32),
     ("bf16", 64, 8, 128, 32, 512), ("bf16", 64, 8, 128, 32, 96),
     ("f16", 40, 40, 128, 16, 512), ("f16", 8, 8, 64, 32, 64),
@@ -201,6 +201,20 @@ def test_decode_small(dtype, h_q, h_kv, d, bs, part, peaked):
     say("  max abs", ea, "max rel", er)
     # zero context -> zero row
     assert np.all(got[0] == 0)
+
+
+@pytest.mark.parametrize("d,bs,part", [(64, 16, 0), (128, 32, 0), (64, 16, 2048)])
+def test_decode_f32_long_ranges(d, bs, part):
+    """fp32 ranges of more than 64 blocks: the block-table window is refilled
+    while the next block's K/V are already requested (contexts on and around
+    the 64-block boundaries, a one-block one, an empty one)."""
+    lens = [64 * bs, 64 * bs + 1, 3 * 64 * bs - 7, 2500, bs, 0]
+    sc = small_scenario("f32", 4, 2, d, bs, seed=9190 + d + bs + part, lens=lens)
+    say("f32 long ranges", d, bs, part, lens)
+    _, _, got, ref, rows = run_both(sc, part)
+    ea, er = H.check_attention(got, ref, "f32", rows)
+    say("  max abs", ea, "max rel", er)
+    assert np.all(got[lens.index(0)] == 0)
 
 
 @pytest.mark.parametrize("dtype,bs", [("bf16", 32), ("f16", 16)])
