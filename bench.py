@@ -1,11 +1,13 @@
 """PagedAttention decode benchmark on one MI355X.
 
-One step = the whole decode hot path for one batch: the host pool appends one
-token per sequence (slot mapping and copy-on-write decisions, C++), block
-tables / lengths / slots go to the device through pinned double buffers,
-pa_copy_blocks runs for any copy-on-write pair, pa_write_kv stores the new
-K/V, and pa_decode (partition kernel + log-sum-exp reduce) computes the
-attention output.  Inputs are resident in HBM before the timed region starts.
+One step = the whole decode hot path for one batch, one pa_decode_step call:
+the host pool appends one token per sequence (slot mapping and copy-on-write
+decisions, C++), block tables / lengths / slots go to the device from a
+pinned staging buffer (one of four, used in turn) through a copy kernel on
+the stream, pa_copy_blocks runs for any copy-on-write pair, and pa_decode
+(partition kernel + log-sum-exp reduce) computes the attention output and
+stores the new K/V in the same launch (pa_write_kv first for fp32).  Inputs
+are resident in HBM before the timed region starts.
 
 Prints one JSON line.  `value` is the effective KV bandwidth of the whole step
 (algorithmic KV bytes read by the step's decode / step time);
