@@ -531,6 +531,24 @@ void decode_part_mfma(
   TableWindow win;
   fill_window(win, bt, t0 / BS, nb_valid, num_blocks, lane);
   int tg = t0;
+  if constexpr (D == 64) {
+    // head dim 64: a group's K/V is half as many bytes, so two groups are
+    // requested per iteration (a wave then has as many bytes in flight as
+    // with head dim 128); they are computed in order, as one at a time
+    for (; tg + 32 < tfull; tg += 64) {
+      GroupTiles<T, D> A, B2;
+      load_group<T, D, BS, NT>(A, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk,
+                               krow, vblk, vslab, g, c, lane);
+      load_group<T, D, BS, NT>(B2, win, bt, tg + 32, nb_valid, num_blocks, kh, vh, blk_stride,
+                               kblk, krow, vblk, vslab, g, c, lane);
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+        compute_group<T, D, false>(A, qop[t], o[t], m[t], l[t], 32, g, scale_log2);
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+        compute_group<T, D, false>(B2, qop[t], o[t], m[t], l[t], 32, g, scale_log2);
+    }
+  }
   for (; tg < tfull; tg += 32) {
     GroupTiles<T, D> A;
     load_group<T, D, BS, NT>(A, win, bt, tg, nb_valid, num_blocks, kh, vh, blk_stride, kblk, krow,
