@@ -1,7 +1,7 @@
 """Drive a synth.Scenario through one side: the oracle side (PoolModel + the
 oracle's NumPy write/copy) or the GPU side (C++ pool + libpa.so kernels).
 
-The driver only sequences operations; it holds no method arithmetic.  Writes
+The harness only sequences operations; it holds no method arithmetic.  Writes
 are batched: pending token writes are flushed before any block copy and before
 any free, so the order of effects on the cache is the scenario's order.
 """
