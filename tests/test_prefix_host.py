@@ -137,6 +137,66 @@ def test_prefix_fuzz_bit_exact_against_model(L, kind, seed, bs):
     assert st["hits"] > 0 and st["evicted"] > 0
 
 
+@pytest.mark.parametrize("kind,seed,bs", [(PC.HASH, 11, 4), (PC.RADIX, 12, 4),
+                                          (PC.HASH, 13, 16), (PC.RADIX, 14, 8)])
+def test_beam_steps_with_token_ids_bit_exact_against_model(L, kind, seed, bs):
+    """Beam search from prompts found in the prefix index, with the token id
+    of every new position passed to the beam step: the blocks the beams fill
+    are indexed as they fill, beams are retired and their ids reused, later
+    prompts hit the beams' blocks; slots, copy-on-write pairs, free list,
+    refcounts, tables and index statistics equal the model's throughout."""
+    rng = random.Random(seed)
+    N = 61
+    order = rng.sample(range(N), N)
+    pool, model = pa.Pool(N, bs, order), PoolModel(N, bs, order)
+    assert pool.enable_prefix_cache(kind) == model.enable_prefix_cache(kind) == 0
+    system = [rng.randrange(40) for _ in range(3 * bs + 1)]
+    families, nxt, stepped = [], 0, 0
+    for it in range(400):
+        r = rng.random()
+        if r < 0.2 or not families:
+            toks = system[:rng.randint(bs, len(system))] + \
+                [rng.randrange(40) for _ in range(rng.randint(0, bs))]
+            a, b = pool.create_cached(nxt, toks), model.create_cached(nxt, toks)
+            assert a[0] == b[0] and a[1] == b[1] and a[2].tolist() == b[2], it
+            if a[0] == 0:
+                families.append([nxt])
+            nxt += 1
+        elif r < 0.88:
+            fi = rng.randrange(len(families))
+            fam = families[fi]
+            W = rng.randint(0, 4)
+            parents = [rng.choice(fam) for _ in range(W)]
+            news = []
+            for _ in range(W):
+                reuse = [o for o in fam if o not in news]
+                if reuse and rng.random() < 0.3:
+                    news.append(rng.choice(reuse))
+                else:
+                    news.append(nxt)
+                    nxt += 1
+            toks = [rng.randrange(40) for _ in range(W)]
+            a = pool.beam_step(fam, parents, news, toks)
+            b = model.beam_step(fam, parents, news, toks)
+            assert a[0] == b[0] and a[1].tolist() == list(b[1]), it
+            assert [tuple(x) for x in a[2].tolist()] == [tuple(x) for x in b[2]], it
+            if a[0] in (0, pa.PA_ERR_NO_BLOCKS):     # the fork-and-retire part ran
+                stepped += a[0] == 0
+                if news:
+                    families[fi] = news
+                else:
+                    families.pop(fi)
+        else:
+            fam = families.pop(rng.randrange(len(families)))
+            for sid in fam:
+                assert pool.free(sid) == model.free_seq(sid) == 0
+        if it % 20 == 0:
+            compare(pool, model)
+    compare(pool, model)
+    st = model.prefix_stats()
+    assert stepped > 50 and st["hits"] > 0 and st["indexed"] > 0
+
+
 def test_prefix_error_paths(L):
     p = pa.Pool(16, 4)
     assert p.create_cached(0, [1, 2, 3])[0] == pa.PA_ERR_INVALID      # no index
