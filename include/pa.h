@@ -349,6 +349,10 @@ pa_status pa_decode_cascade(void* out, const void* q, const void* k_cache, const
  * work is on `stream`.  Not for graph capture (the pool step runs on the
  * host).
  *
+ *   tokens        host int32 [num_seqs] token id of each new position, or NULL;
+ *                 with ids the append is pa_seq_append_tokens, so sequences
+ *                 that a prefix index tracks keep feeding it (without, it is
+ *                 pa_seq_append_batch, which ends that tracking)
  *   host_staging  pinned host memory (hipHostMalloc), >=
  *                 pa_decode_step_staging_size() bytes, 16-byte aligned; a
  *                 small kernel on `stream` reads it through its device
@@ -366,7 +370,8 @@ pa_status pa_decode_cascade(void* out, const void* q, const void* k_cache, const
  * memory; nothing is allocated.
  */
 size_t pa_decode_step_staging_size(int num_seqs, int max_blocks_per_seq);
-pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_seqs, const void* k_new,
+pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_seqs,
+                         const int32_t* tokens, const void* k_new,
                          const void* v_new, void* k_cache, void* v_cache, int num_blocks,
                          int num_kv_heads, int head_dim, int block_size, const void* q,
                          void* out, int num_q_heads, float scale, int partition_size,
@@ -376,7 +381,8 @@ pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_seqs, const
 
 /*
  * pa_beam_decode_step — one beam-search iteration in one call:
- * pa_seq_beam_step(old_beams, parents, new_beams) in the pool, then, as in
+ * pa_seq_beam_step(old_beams, parents, new_beams, tokens) in the pool (tokens:
+ * host int32 [n_new] or NULL, as there), then, as in
  * pa_decode_step (same staging and fused block write), the staging
  * copy, pa_copy_blocks of its pairs, the block write of k_new / v_new (device
  * [n_new][H_kv][d], in new_beams order) and pa_decode of q into out (device
@@ -388,7 +394,8 @@ pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_seqs, const
  */
 pa_status pa_beam_decode_step(pa_pool* pool, const int64_t* old_beams, int n_old,
                               const int64_t* parents, const int64_t* new_beams, int n_new,
-                              const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* tokens, const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache,
                               int num_blocks, int num_kv_heads, int head_dim, int block_size,
                               const void* q, void* out, int num_q_heads, float scale,
                               int partition_size, int max_blocks_per_seq, void* host_staging,

@@ -63,11 +63,11 @@ SIGNATURES = {
     "pa_seq_append_tokens": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp]),
     "pa_prefix_stats": (_i, [_vp, _vp]),
     "pa_seq_beam_step": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp]),
-    "pa_beam_decode_step": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
-                                 _vp, _vp, _i, _f, _i, _i, _vp, _vp, _sz, _vp, _sz, _i, _vp]),
+    "pa_beam_decode_step": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                 _i, _vp, _vp, _i, _f, _i, _i, _vp, _vp, _sz, _vp, _sz, _i, _vp]),
     "pa_decode_step_staging_size": (_sz, [_i, _i]),
-    "pa_decode_step": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _f,
-                            _i, _i, _vp, _vp, _sz, _vp, _sz, _i, _vp]),
+    "pa_decode_step": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i,
+                            _f, _i, _i, _vp, _vp, _sz, _vp, _sz, _i, _vp]),
     "pa_pool_create": (_i, [_i, _i, _vp, _c.POINTER(_vp)]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_seq_create": (_i, [_vp, _i64]),
@@ -435,20 +435,34 @@ def pa_decode_step_staging_size(num_seqs: int, max_blocks_per_seq: int) -> int:
     return int(lib().pa_decode_step_staging_size(num_seqs, max_blocks_per_seq))
 
 
+def _token_ids(tokens, n: int):
+    """Optional token ids of the appended positions: None, or n ids (int32)."""
+    if tokens is None:
+        return None
+    tk = np.ascontiguousarray(tokens, dtype=np.int32)
+    if tk.ndim != 1 or tk.size != n:
+        raise ValueError(f"tokens must be {n} ids, one per appended position")
+    return tk
+
+
 def pa_decode_step(pool: "Pool", seqs: np.ndarray, k_new, v_new, k_cache, v_cache, q, out,
                    scale: float, partition_size: int, max_blocks_per_seq: int, host_staging,
-                   dev_staging, workspace, stream=None):
+                   dev_staging, workspace, stream=None, tokens=None):
     """seqs: int64 numpy array; host_staging: pinned uint8 CPU tensor; dev_staging,
-    workspace: uint8 GPU tensors; the rest GPU tensors as for pa_write_kv / pa_decode."""
+    workspace: uint8 GPU tensors; the rest GPU tensors as for pa_write_kv / pa_decode.
+    tokens: optional token id of each sequence's new position (a prefix index
+    attached to the pool then keeps indexing the blocks these sequences fill)."""
     nb, H_kv, bs, d, B, H_q = _check_decode_io(out, q, k_cache, v_cache)
     seqs = _seq_ids(seqs)
     if seqs.size != B:
         raise ValueError(f"{seqs.size} sequence ids for {B} query rows")
+    tk = _token_ids(tokens, B)
     _check_new_kv(k_new, v_new, k_cache, B, H_kv, d)
     if not host_staging.is_pinned():
         raise ValueError("host_staging must be pinned host memory")
     sbytes = min(_nbytes(host_staging), _nbytes(dev_staging))
-    st = lib().pa_decode_step(pool._h, _np_ptr(seqs), B, _dev_ptr(k_new, "k_new"),
+    st = lib().pa_decode_step(pool._h, _np_ptr(seqs), B, None if tk is None else _np_ptr(tk),
+                              _dev_ptr(k_new, "k_new"),
                               _dev_ptr(v_new, "v_new"), _dev_ptr(k_cache, "k_cache"),
                               _dev_ptr(v_cache, "v_cache"), nb, H_kv, d, bs, _dev_ptr(q, "q"),
                               _dev_ptr(out, "out"), H_q, float(scale), partition_size,
@@ -462,10 +476,11 @@ def pa_decode_step(pool: "Pool", seqs: np.ndarray, k_new, v_new, k_cache, v_cach
 def pa_beam_decode_step(pool: "Pool", old_beams, parents, new_beams, k_new, v_new, k_cache,
                         v_cache, q, out, scale: float, partition_size: int,
                         max_blocks_per_seq: int, host_staging, dev_staging, workspace,
-                        stream=None):
+                        stream=None, tokens=None):
     """One beam-search iteration in one native call (pool beam step, staging copy,
     copy-on-write, block write, decode).  Ids: int64 numpy arrays; k_new, v_new
-    [len(new_beams)][H_kv][d], q / out [len(new_beams)][H_q][d] GPU tensors."""
+    [len(new_beams)][H_kv][d], q / out [len(new_beams)][H_q][d] GPU tensors;
+    tokens: optional token id of each new beam's new position."""
     nb, H_kv, bs, d, B, H_q = _check_decode_io(out, q, k_cache, v_cache)
     old = _seq_ids(old_beams, "old_beams")
     par = _seq_ids(parents, "parents")
@@ -475,11 +490,13 @@ def pa_beam_decode_step(pool: "Pool", old_beams, parents, new_beams, k_new, v_ne
     if new.size != B:
         raise ValueError(f"{new.size} new beams for {B} query rows")
     _check_new_kv(k_new, v_new, k_cache, B, H_kv, d)
+    tk = _token_ids(tokens, B)
     if not host_staging.is_pinned():
         raise ValueError("host_staging must be pinned host memory")
     sbytes = min(_nbytes(host_staging), _nbytes(dev_staging))
     st = lib().pa_beam_decode_step(pool._h, _np_ptr(old), old.size, _np_ptr(par), _np_ptr(new),
-                                   new.size, _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
+                                   new.size, None if tk is None else _np_ptr(tk),
+                                   _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
                                    _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
                                    nb, H_kv, d, bs, _dev_ptr(q, "q"), _dev_ptr(out, "out"), H_q,
                                    float(scale), partition_size, max_blocks_per_seq,

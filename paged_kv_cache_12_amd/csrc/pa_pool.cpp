@@ -667,4 +667,4 @@ PA_EXPORT const char* pa_status_str(int status) {
   }
 }
 
-PA_EXPORT int pa_abi_version(void) { return 4; }
+PA_EXPORT int pa_abi_version(void) { return 5; }

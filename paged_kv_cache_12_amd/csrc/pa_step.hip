@@ -206,8 +206,9 @@ pa_status launch_step(pa_pool* pool, const StepDev& a, const int64_t* seqs, int 
 }  // namespace
 
 PA_EXPORT pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_seqs,
-                                   const void* k_new, const void* v_new, void* k_cache,
-                                   void* v_cache, int num_blocks, int num_kv_heads, int head_dim,
+                                   const int32_t* tokens, const void* k_new, const void* v_new,
+                                   void* k_cache, void* v_cache, int num_blocks,
+                                   int num_kv_heads, int head_dim,
                                    int block_size, const void* q, void* out, int num_q_heads,
                                    float scale, int partition_size, int max_blocks_per_seq,
                                    void* host_staging, void* dev_staging, size_t staging_bytes,
@@ -232,18 +233,24 @@ PA_EXPORT pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int num_s
   if (st != PA_OK) return st;
   const StagingLayout L = staging_layout(num_seqs, max_blocks_per_seq);
   char* h = static_cast<char*>(host_staging);
-  // host pool: one new position per sequence (all-or-nothing)
+  // host pool: one new position per sequence (all-or-nothing); with token
+  // ids, sequences a prefix index tracks keep feeding it
   int npairs = 0;
-  st = pa_seq_append_batch(pool, seqs, num_seqs, 1, reinterpret_cast<int64_t*>(h + L.slots),
-                           reinterpret_cast<int32_t*>(h + L.pairs), &npairs);
+  st = tokens ? pa_seq_append_tokens(pool, seqs, num_seqs, tokens, 1,
+                                     reinterpret_cast<int64_t*>(h + L.slots),
+                                     reinterpret_cast<int32_t*>(h + L.pairs), &npairs)
+              : pa_seq_append_batch(pool, seqs, num_seqs, 1,
+                                    reinterpret_cast<int64_t*>(h + L.slots),
+                                    reinterpret_cast<int32_t*>(h + L.pairs), &npairs);
   if (st != PA_OK) return st;
   return launch_step(pool, a, seqs, num_seqs, npairs);
 }
 
 PA_EXPORT pa_status pa_beam_decode_step(pa_pool* pool, const int64_t* old_beams, int n_old,
                                         const int64_t* parents, const int64_t* new_beams,
-                                        int n_new, const void* k_new, const void* v_new,
-                                        void* k_cache, void* v_cache, int num_blocks,
+                                        int n_new, const int32_t* tokens, const void* k_new,
+                                        const void* v_new, void* k_cache, void* v_cache,
+                                        int num_blocks,
                                         int num_kv_heads, int head_dim, int block_size,
                                         const void* q, void* out, int num_q_heads, float scale,
                                         int partition_size, int max_blocks_per_seq,
@@ -271,7 +278,7 @@ PA_EXPORT pa_status pa_beam_decode_step(pa_pool* pool, const int64_t* old_beams,
   const StagingLayout L = staging_layout(n_new > 0 ? n_new : 1, max_blocks_per_seq);
   char* h = static_cast<char*>(host_staging);
   int npairs = 0;
-  pa_status st = pa_seq_beam_step(pool, old_beams, n_old, parents, new_beams, n_new, nullptr,
+  pa_status st = pa_seq_beam_step(pool, old_beams, n_old, parents, new_beams, n_new, tokens,
                                   n_new > 0 ? reinterpret_cast<int64_t*>(h + L.slots) : nullptr,
                                   n_new > 0 ? reinterpret_cast<int32_t*>(h + L.pairs) : nullptr,
                                   &npairs);

@@ -50,7 +50,7 @@ def test_status_strings(L):
     assert pa.status_str(3) == "not enough free blocks"
     assert pa.status_str(6) == "request exceeds the fixed no-allocation scratch"
     assert pa.status_str(99) == "unknown status"
-    assert L.pa_abi_version() == 4
+    assert L.pa_abi_version() == 5
 
 
 def test_kv_bytes_per_token_matches_closed_form(L):
@@ -341,7 +341,7 @@ def _step(L, pool, seqs, **kw):
              ws_bytes=0, dt=2)
     a.update(kw)
     s = np.ascontiguousarray(seqs, dtype=np.int64)
-    return L.pa_decode_step(pool._h, s.ctypes.data_as(ctypes.c_void_p), s.size, a["k_new"],
+    return L.pa_decode_step(pool._h, s.ctypes.data_as(ctypes.c_void_p), s.size, None, a["k_new"],
                             a["v_new"], a["kc"], a["vc"], a["nb"], a["H_kv"], a["d"], a["bs"],
                             a["q"], a["out"], a["H_q"], a["scale"], a["part"], a["maxb"],
                             a["hs"], a["ds"], a["sbytes"], a["ws"], a["ws_bytes"], a["dt"], None)

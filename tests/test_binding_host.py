@@ -115,6 +115,27 @@ def test_decode_step_converts_seq_ids_to_int64():
         call_step(np.arange(3, dtype=np.int32), out, q, k, v, kn, vn)
 
 
+def test_steps_refuse_token_ids_of_the_wrong_count():
+    """Token ids: one per appended position, checked before the pool or any
+    pointer is touched."""
+    out, q, k, v, kn, vn = step_args()
+    pool = pa.Pool(NB, BS)
+    stage = torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="tokens"):
+        pa.pa_decode_step(pool, np.arange(3), kn, vn, k, v, q, out, 0.125, 0, 2, stage, stage,
+                          stage, tokens=[1, 2])
+    with pytest.raises(ValueError, match="tokens"):
+        pa.pa_decode_step(pool, np.arange(3), kn, vn, k, v, q, out, 0.125, 0, 2, stage, stage,
+                          stage, tokens=[[1], [2], [3]])
+    with pytest.raises(ValueError, match="tokens"):
+        pa.pa_beam_decode_step(pool, [0], [0, 0, 0], [1, 2, 3], kn, vn, k, v, q, out, 0.125, 0,
+                               2, stage, stage, stage, tokens=[5])
+    # the right count passes every check and reaches the pinned-memory one
+    with pytest.raises(ValueError, match="pinned"):
+        pa.pa_decode_step(pool, np.arange(3), kn, vn, k, v, q, out, 0.125, 0, 2, stage, stage,
+                          stage, tokens=[1, 2, 3])
+
+
 def test_beam_step_refuses_mismatches():
     out, q, k, v, kn, vn = step_args(B=4)
     pool = pa.Pool(NB, BS)

@@ -109,15 +109,20 @@ def test_beam_search_matches_oracle(dtype, bs, part, W):
     assert copies > 0
 
 
-@pytest.mark.parametrize("dtype,part", [("bf16", 0), ("f16", 64)])
-def test_beam_decode_step_matches_oracle(dtype, part):
+@pytest.mark.parametrize("dtype,part,kind", [("bf16", 0, 0), ("f16", 64, 0), ("bf16", 64, 1),
+                                             ("f16", 0, 2)])
+def test_beam_decode_step_matches_oracle(dtype, part, kind):
+    """One-call beam steps against the pool model and the oracle.  kind > 0:
+    the prompts come through a prefix index (1 chain hash, 2 radix tree)
+    and each step passes the new positions' token ids, so the index keeps
+    tracking the beams; its statistics equal the model's at the end."""
     import torch
     import paged_kv_cache_12_amd as pa
     from oracle import attention as A
     from oracle.pool_model import PoolModel
     from paged_kv_cache_12_amd.manager import PagedKVCache, storage_to_torch, torch_to_storage
     from test_gpu_parity import to_f64
-    say("beam_decode_step", dtype, part)
+    say("beam_decode_step", dtype, part, kind)
     rng = random.Random(77 + part)
     Hq, Hkv, d, bs, W, P = 16, 4, 128, 16, 3, 4
     N = 256
@@ -136,15 +141,33 @@ def test_beam_decode_step_matches_oracle(dtype, part):
         return storage_to_torch(a, dtype).cuda()
 
     beams = []
+    if kind:
+        gpu.enable_prefix_cache(kind)
+        assert model.enable_prefix_cache(kind) == 0
+        system = [rng.randrange(1000) for _ in range(40)]
     for g in range(P):
         n = rng.randint(5, 200)
-        kv = synth.normal_array(41, (g, 1), (n, Hkv, d), dtype)
-        vv = synth.normal_array(41, (g, 2), (n, Hkv, d), dtype)
-        gpu.create(g)
-        gpu.append([g], n, dev(kv), dev(vv))
-        model.create(g)
-        _, slots, _ = model.append(g, n)
-        A.write_kv(kc, vc, kv, vv, np.asarray(slots))
+        if kind:
+            t = system[:rng.randint(16, 40)] + [rng.randrange(1000) for _ in range(n)]
+            kvs = {}
+
+            def k_of(a, b, t=t, kvs=kvs):
+                kvs["k"], kvs["v"] = synth.prefix_values(t, a, b, Hkv, d, dtype)
+                return dev(kvs["k"])
+
+            c = gpu.create_cached(g, t, k_of, lambda a, b, kvs=kvs: dev(kvs["v"]))
+            so, co, slots = model.create_cached(g, t)
+            assert so == 0 and co == c
+            if len(slots):
+                A.write_kv(kc, vc, kvs["k"], kvs["v"], np.asarray(slots))
+        else:
+            kv = synth.normal_array(41, (g, 1), (n, Hkv, d), dtype)
+            vv = synth.normal_array(41, (g, 2), (n, Hkv, d), dtype)
+            gpu.create(g)
+            gpu.append([g], n, dev(kv), dev(vv))
+            model.create(g)
+            _, slots, _ = model.append(g, n)
+            A.write_kv(kc, vc, kv, vv, np.asarray(slots))
         beams.append(g)
     maxb = 32
     sbytes = pa.pa_decode_step_staging_size(P * W, maxb)
@@ -164,11 +187,12 @@ def test_beam_decode_step_matches_oracle(dtype, part):
         q = synth.normal_array(42, (step, 3), (B, Hq, d), dtype)
         qd = dev(q)
         out = torch.empty_like(qd)
+        toks = [rng.randrange(1000) for _ in news] if kind else None
         pa.pa_beam_decode_step(gpu.pool, beams, parents, news, dev(kn), dev(vn), gpu.k_cache,
                                gpu.v_cache, qd, out, 1.0 / np.sqrt(d), part, maxb,
-                               hs[step % 2], ds, ws)
+                               hs[step % 2], ds, ws, tokens=toks)
         torch.cuda.synchronize()
-        so, sl_o, pr_o = model.beam_step(beams, parents, news)
+        so, sl_o, pr_o = model.beam_step(beams, parents, news, toks)
         assert so == 0
         if pr_o:
             A.copy_blocks(kc, vc, pr_o)
@@ -187,3 +211,6 @@ def test_beam_decode_step_matches_oracle(dtype, part):
     assert np.array_equal(kf[1:1 + N].view(ib), kc.view(ib))
     assert np.array_equal(vf[1:1 + N].view(ib), vc.view(ib))
     assert copies > 0
+    if kind:
+        ps = model.prefix_stats()
+        assert gpu.pool.prefix_stats() == ps and ps["hits"] > 0 and ps["indexed"] > 0

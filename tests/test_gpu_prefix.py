@@ -131,12 +131,15 @@ def test_prefix_stream_matches_oracle(kind, dtype, bs, part):
     say("  live", len(live), "max abs", ea, "max rel", er)
 
 
-@pytest.mark.parametrize("kind", [1, 2])
-def test_prefix_hits_decode_steps(kind):
+@pytest.mark.parametrize("kind,with_tokens", [(1, False), (2, False), (1, True), (2, True)])
+def test_prefix_hits_decode_steps(kind, with_tokens):
     """Requests that hit a long cached system prompt (two tenants by salt),
-    then one-call decode steps over all of them: plain appends (which end
-    the index's tracking), and the cascade over the hits, whose shared
-    prefixes exceed 512 tokens; against the oracle, caches bit-exact."""
+    then one-call decode steps over all of them, and the cascade over the
+    hits, whose shared prefixes exceed 512 tokens; against the oracle, caches
+    bit-exact.  Without token ids the steps' appends end the index's tracking;
+    with them the blocks the steps fill are indexed as they fill, and a later
+    request that repeats a sequence's whole history finds them (the pool's
+    index equal to the model's throughout)."""
     import torch
     import paged_kv_cache_12_amd as pa
     from oracle import attention as A
@@ -144,7 +147,7 @@ def test_prefix_hits_decode_steps(kind):
     from paged_kv_cache_12_amd.manager import PagedKVCache, storage_to_torch, torch_to_storage
     from test_gpu_parity import to_f64
     dtype, bs, part, Hq, Hkv, d = "bf16", 16, 512, 16, 4, 128
-    say("prefix hits + decode steps", "hash" if kind == 1 else "radix")
+    say("prefix hits + decode steps", "hash" if kind == 1 else "radix", with_tokens)
     rng = random.Random(500 + kind)
     N = 500
     order = np.random.default_rng(50 + kind).permutation(N).astype(np.int32)
@@ -161,11 +164,12 @@ def test_prefix_hits_decode_steps(kind):
     vc.view(ib)[...] = synth.poison_bits(dtype)
     dev = lambda a: storage_to_torch(a, dtype).cuda()
     system = [rng.randrange(30000) for _ in range(1100)]
-    live, cached = [], 0
+    live, cached, history = [], 0, {}
     for sid in range(12):
         t = system[:rng.randint(800, 1100)] + [rng.randrange(30000)
                                                for _ in range(rng.randint(1, 60))]
         salt = b"tenant-b" if sid % 4 == 3 else b""
+        history[sid] = (list(t), salt)
         kv = {}
 
         def k_of(a, b, t=t, kv=kv):
@@ -204,16 +208,22 @@ def test_prefix_hits_decode_steps(kind):
                          pa.pa_decode_workspace_size(B, Hq, d, maxb * bs, part), 256),
                      dtype=torch.uint8, device="cuda")
     seqs = np.asarray(live, dtype=np.int64)
-    for step in range(3):
+    for step in range(20 if with_tokens else 3):
         kn = synth.normal_array(60 + kind, (step, 1), (B, Hkv, d), dtype)
         vn = synth.normal_array(60 + kind, (step, 2), (B, Hkv, d), dtype)
         q = synth.normal_array(60 + kind, (step, 3), (B, Hq, d), dtype)
         qd = dev(q)
         out = torch.empty_like(qd)
+        toks = [rng.randrange(30000) for _ in live] if with_tokens else None
         pa.pa_decode_step(gpu.pool, seqs, dev(kn), dev(vn), gpu.k_cache, gpu.v_cache, qd, out,
-                          1.0 / np.sqrt(d), part, maxb, hs[step % 2], ds, ws)
+                          1.0 / np.sqrt(d), part, maxb, hs[step % 2], ds, ws, tokens=toks)
         torch.cuda.synchronize()
-        so, sl_o, pr_o = model.append_batch(live, 1)
+        if with_tokens:
+            so, sl_o, pr_o = model.append_tokens(live, [[t_] for t_ in toks])
+            for s_, t_ in zip(live, toks):
+                history[s_][0].append(t_)
+        else:
+            so, sl_o, pr_o = model.append_batch(live, 1)
         assert so == 0
         if pr_o:
             A.copy_blocks(kc, vc, pr_o)
@@ -223,6 +233,16 @@ def test_prefix_hits_decode_steps(kind):
         ea, er = H.check_attention(to_f64(out, dtype), ref, dtype, range(B))
         say("  step", step, "max abs", ea, "max rel", er)
     assert gpu.pool.prefix_stats() == model.prefix_stats()
+    if with_tokens:
+        # a request repeating a sequence's whole history (prompt and the
+        # steps' tokens) finds the blocks the steps filled
+        full, salt = max(history.values(), key=lambda h: len(h[0]))
+        got = gpu.pool.create_cached(901, full + [7], salt)
+        exp = model.create_cached(901, full + [7], salt)
+        assert got[0] == exp[0] == 0 and got[1] == exp[1], (got[:2], exp[:2])
+        # every full block of the history, also the ones filled by the steps
+        assert got[1] == (len(full) // bs) * bs > ((len(full) - 20) // bs) * bs
+        assert gpu.pool.prefix_stats() == model.prefix_stats()
     kf, vf = torch_to_storage(gpu.k_full, dtype), torch_to_storage(gpu.v_full, dtype)
     assert np.array_equal(kf[1:1 + N].view(ib), kc.view(ib))
     assert np.array_equal(vf[1:1 + N].view(ib), vc.view(ib))
